@@ -1,0 +1,75 @@
+"""The fp64 oracle against facts fixed by the pages and by mathematics.
+
+Every check lives in ``oracle_pins.py`` so that ``test_oracle_mutants.py``
+can run the same checks against copies of the oracle with a planted mistake.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from io_aware_attention_flash_amd.inputs import WORKLOADS, make_qkv
+
+
+def _attn(q, k, v, causal, scale, rows=None):
+    return oracle.attn_oracle(q, k, v, causal=causal, scale=scale, rows=rows)
+
+
+@pytest.mark.parametrize("check", oracle_pins.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check(_attn)
+
+
+def test_online_variant_reproduces_exercise5_state():
+    """The online variant's state after each block is the exercise's worked
+    state (alpha, l and un-normalised O after block 2)."""
+    import json
+    import os
+    g = json.load(open(os.path.join(oracle_pins.GOLDEN, "exercise5_online_softmax.json")))
+    trace = []
+    q = np.ones((1, 1))
+    k = np.array(g["scores"]).reshape(2, 1)
+    v = np.array(g["values"]).reshape(2, 1)
+    o, lse = oracle.attn_online_np(q, k, v, False, 1.0, block=1, trace=trace)
+    b1, b2 = trace
+    assert (b1["m"], b1["l"], b1["O"][0]) == (g["after_block1"]["m"], g["after_block1"]["l"],
+                                              g["after_block1"]["O"])
+    assert b2["m"] == g["after_block2"]["m"]
+    assert abs(b2["alpha"] - g["after_block2"]["alpha"]) <= 1e-16
+    assert abs(b2["l"] - g["after_block2"]["l"]) <= 1e-15
+    assert abs(b2["O"][0] - g["after_block2"]["O"]) <= 1e-15
+    assert abs(o[0, 0] - g["O_normalised"]) <= 1e-15
+    assert abs(lse[0] - g["lse"]) <= 1e-15
+
+
+def test_oracle_rejects_bad_rows():
+    q = np.zeros((1, 1, 4, 2))
+    with pytest.raises(RuntimeError):
+        oracle.attn_oracle(q, q, q, rows=[4])
+    with pytest.raises(RuntimeError):
+        oracle.attn_oracle(q, q, q, rows=[-1])
+
+
+def test_oracle_on_workload_inputs_small_sample():
+    """The oracle runs on the real input recipe (bf16 values upcast) and
+    returns finite, hull-bounded rows for the large-logit workload."""
+    w = WORKLOADS["b1h16_n16384_d128_bf16_sigma3_causal"]
+    q, k, v = make_qkv(1, 1, 1024, w.d, w.dtype, w.sigma, seed=0)
+    rows = [0, 1, 511, 1023]
+    o, lse = oracle.attn_oracle(q, k, v, causal=True, scale=w.scale, rows=rows)
+    vv = v.double().numpy()[0, 0]
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.array_equal(o[0], vv[0])
+    for r, i in enumerate(rows):
+        assert np.all(o[r] <= vv[:i + 1].max(axis=0) + 1e-12)
+        assert np.all(o[r] >= vv[:i + 1].min(axis=0) - 1e-12)
+
+
+def test_input_recipe_is_seeded_and_rounded():
+    a = make_qkv(1, 2, 8, 16, "bf16", 3.0, seed=5)
+    b = make_qkv(1, 2, 8, 16, "bf16", 3.0, seed=5)
+    c = make_qkv(1, 2, 8, 16, "bf16", 3.0, seed=6)
+    assert all(x.dtype.is_floating_point and x.shape == (1, 2, 8, 16) for x in a)
+    assert all((x == y).all() for x, y in zip(a, b))
+    assert not (a[0] == c[0]).all()
+    assert not (a[0] == a[1]).all()
