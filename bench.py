@@ -1,0 +1,173 @@
+"""Benchmark of the attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--out-dtype f32|in] [--no-cpu-baseline]
+
+A step is one attn_fwd call (the whole forward: QK^T, masking, online
+softmax, P.V, normalisation, LSE) over one batch of seeded synthetic input
+that is already resident in HBM. W untimed steps, then exactly K timed steps
+bracketed by torch.cuda.synchronize(); the kernel duration comes from HIP
+events recorded on the stream the kernel is launched on.
+
+Prints one JSON line. FLOPs count the two N x N x d contractions per head,
+halved when causal: 4*B*H*N^2*d (/2). Algorithmic bytes read Q, K, V once
+and write O and LSE once.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from io_aware_attention_flash_amd import binding  # noqa: E402
+from io_aware_attention_flash_amd import build as hipbuild  # noqa: E402
+from io_aware_attention_flash_amd.inputs import HEADLINE, WORKLOADS, workload_qkv  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+METRIC = "attention fwd TFLOP/s + % bf16 MFMA peak (causal, N=4096, d=128)"
+KERNEL_SRC = os.path.join(ROOT, "io_aware_attention_flash_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_digest():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload, out_dtype):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, or None when absent or taken on a different kernel source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    ent = rec.get("entries", {}).get("%s/%s" % (workload, out_dtype))
+    if not ent or ent.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, budget_s=12.0):
+    """Time the fp64 oracle on whole heads of the same inputs until about
+    `budget_s` seconds of CPU work; report the FLOP rate of that sample."""
+    import numpy as np
+    import oracle
+    oracle.build_oracle()
+    threads = oracle.oracle_threads()
+    B, H, N, d = q.shape
+    heads_done, flops, elapsed = 0, 0.0, 0.0
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        args = [x[b:b + 1, h:h + 1] for x in (q, k, v)]
+        t0 = time.perf_counter()
+        oracle.attn_oracle(*args, causal=w.causal, scale=w.scale)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        n_keys = np.arange(1, N + 1, dtype=np.float64) if w.causal else np.full(N, float(N))
+        flops += float(4.0 * d * n_keys.sum())
+        if elapsed >= budget_s:
+            break
+    # Scale the sample's rate to the metric's FLOP convention (the causal
+    # half-count); the sample's exact triangle count is what was executed.
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads of %s (fp64 three-pass oracle, %.1f s, %.3g FLOP)"
+                      % (heads_done, B * H, w.name, elapsed, flops),
+            "seconds": round(elapsed, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--out-dtype", default="f32", choices=["f32", "in"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes in the design doc). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not os.path.exists(binding.LIB_PATH):
+        hipbuild.build()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = WORKLOADS[args.workload]
+    qc, kc, vc = workload_qkv(w, seed=0)
+    q, k, v = qc.to(dev), kc.to(dev), vc.to(dev)
+    out_dtype = torch.float32 if args.out_dtype == "f32" else w.torch_dtype
+    out_name = "f32" if args.out_dtype == "f32" else w.dtype
+    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def step():
+        binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out_dtype=out_dtype, out=o,
+                         lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    alg_bytes = w.algorithmic_bytes(out_name)
+    traffic = measured_traffic(w.name, out_name)
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) Q/K/V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "in_dtype": w.dtype, "out_dtype": out_name,
+                   "sigma": w.sigma, "scale": w.scale},
+        "pct_of_bf16_peak": round(100.0 * tflops / PEAK_TFLOPS["bf16"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": traffic},
+        "hbm": {"algorithmic_bytes": alg_bytes,
+                "achieved_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                "peak_GBps": PEAK_HBM_GBS},
+        "wall_s_timed_region": round(wall, 4),
+        "flops_per_step": flops,
+    }
+    if w.causal:
+        res["flops_exact_triangle_per_step"] = w.flops_exact_causal()
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

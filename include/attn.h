@@ -1,0 +1,104 @@
+/*
+ * attn.h -- C ABI of the gfx950 (MI355X) attention forward library
+ * (libattn_fwd.so). Plain C: no C++ types, no exceptions across the
+ * boundary, no torch types. Device pointers are HIP device pointers; the
+ * stream is a hipStream_t passed as void* (NULL = the default stream).
+ *
+ * Operation (the FlashAttention forward of "4.4 Writing GPU Kernels with
+ * Triton", section "Kernel 4: A Simplified FlashAttention", whose driver
+ * takes q, k, v of shape (B, H, N, d) and returns O and the per-row
+ * logsumexp L): for every batch b, head h and query row i
+ *
+ *   s_ij   = scale * sum_c Q[b,h,i,c] K[b,h,j,c]          j in A(i)
+ *   O[b,h,i,:] = sum_{j in A(i)} softmax_j(s_i.) V[b,h,j,:]
+ *   LSE[b,h,i] = ln sum_{j in A(i)} exp(s_ij)             (natural log)
+ *
+ * where A(i) = {0, ..., N-1}, or {0, ..., i} when causal (query i sees only
+ * keys j <= i -- that page's causal mask). The N x N score matrix is never
+ * written to memory: the kernels stream K/V tiles and keep the online
+ * softmax state (running maximum, running sum, rescaled output) on chip,
+ * following that page's section "The Online Softmax Recurrence".
+ */
+#ifndef ATTN_FWD_ATTN_H
+#define ATTN_FWD_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+  ATTN_F32 = 0,  /* IEEE binary32 */
+  ATTN_F16 = 1,  /* IEEE binary16 */
+  ATTN_BF16 = 2  /* bfloat16 */
+} attn_dtype;
+
+/* Status codes. Nothing is printed and nothing aborts. */
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,         /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,        /* B, H or N < 1, or a size beyond the limits below */
+  ATTN_ERR_UNSUPPORTED = 3,  /* head dim or dtype combination not built */
+  ATTN_ERR_SCALE = 4,        /* scale is NaN, infinite or negative */
+  ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+} attn_status;
+
+/* Version of this ABI (bumped on any incompatible change). */
+#define ATTN_ABI_VERSION 1
+
+/*
+ * attn_fwd -- enqueue the attention forward on `stream`.
+ *
+ * q, k, v : device, [B][H][N][d] contiguous (row-major), element type in_dtype.
+ * o       : device, [B][H][N][d] contiguous, element type out_dtype; written.
+ * lse     : device, [B][H][N] contiguous fp32; written with the natural-log
+ *           logsumexp of each row's scaled scores (the value the backward
+ *           pass needs; "Kernel 4", notes on the saved L).
+ * B, H, N : batch, heads, sequence length (queries = keys = N).
+ * d       : head dimension, 64 or 128.
+ * causal  : non-zero -> query i attends to keys j <= i only.
+ * scale   : softmax scale, finite and >= 0; callers wanting the pages'
+ *           default pass 1/sqrt(d). (A scale of exactly 0 is applied as the
+ *           smallest normal fp32 number: every score then rounds to the
+ *           same exponent and the weights are exactly uniform.)
+ * in_dtype / out_dtype : supported pairs are
+ *           (BF16, BF16) (BF16, F32) (F16, F16) (F16, F32) (F32, F32).
+ *           bf16 and fp16 inputs are multiplied on the matrix cores with fp32
+ *           accumulation; the softmax weights P enter the P.V product as
+ *           fp16 (for bf16 inputs V is converted to fp16, which is exact for
+ *           |v| in [2^-14, 65504]); softmax statistics are fp32. fp32 inputs
+ *           are computed in fp32 throughout.
+ * stream  : hipStream_t (or NULL). The call only enqueues work and does not
+ *           synchronise; a fault during execution surfaces at the caller's
+ *           next synchronisation.
+ *
+ * Limits: N <= 2^24, B*H <= 2^24, and the launch grid ceil(N/128)*B*H must
+ * fit in 2^31 - 1 workgroups; otherwise ATTN_ERR_SHAPE.
+ * Ownership: the caller allocates and owns all five buffers; the library
+ * allocates nothing and keeps no per-call state, so concurrent calls on
+ * different streams are safe. o and lse must not alias q, k or v (not
+ * checked).
+ * Errors: every argument is validated before any HIP call is made, so the
+ * error paths need no GPU. ATTN_ERR_HIP carries the raw hipError_t in
+ * attn_last_hip_error().
+ */
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
+                     int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                     attn_dtype in_dtype, attn_dtype out_dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *attn_status_string(attn_status s);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+/* Raw hipError_t behind the last ATTN_ERR_HIP returned on this thread (0 if none). */
+int attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_ATTN_H */

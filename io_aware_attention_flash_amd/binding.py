@@ -1,0 +1,108 @@
+"""Thin ctypes binding of libattn_fwd.so (the C ABI in include/attn.h).
+
+Argument marshalling only: every step of the attention forward runs in the
+library's HIP kernels. torch supplies the device buffers and the stream.
+There is no fallback: if the library cannot be loaded the call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+
+# attn_dtype / attn_status values of include/attn.h
+ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
+          4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP"}
+EXPORTS = ("attn_fwd", "attn_status_string", "attn_abi_version", "attn_last_hip_error")
+
+_TORCH_TO_ATTN = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, msg))
+        self.status = status
+
+
+def load_library(path=LIB_PATH):
+    """Open the library and declare its signatures. Raises if it is missing."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("HIP attention library not built: %s is missing "
+                           "(run python -m io_aware_attention_flash_amd.build)" % path)
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_abi_version.restype = ctypes.c_int
+    lib.attn_abi_version.argtypes = []
+    lib.attn_last_hip_error.restype = ctypes.c_int
+    lib.attn_last_hip_error.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, scale,
+                 in_dtype, out_dtype, stream=None):
+    """Direct call of the C entry point with integer pointers; returns the status."""
+    return load_library().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(N),
+                                   int(d), int(bool(causal)), float(scale), int(in_dtype),
+                                   int(out_dtype), stream)
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=None):
+    """Attention forward of [B, H, N, d] tensors on the current HIP stream.
+
+    scale defaults to 1/sqrt(d); out_dtype defaults to the input dtype
+    (torch.float32 is also accepted for bf16/fp16 inputs). Returns (o, lse)
+    with lse [B, H, N] fp32 natural-log logsumexp. Preallocated `out`/`lse`
+    may be passed to avoid allocation.
+    """
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d] of one shape")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_TO_ATTN:
+        raise ValueError("q, k, v must share one dtype among float32/float16/bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous [B, H, N, d] tensor of out_dtype on q's device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous [B, H, N] float32 tensor on q's device")
+    if out_dtype not in _TORCH_TO_ATTN:
+        raise ValueError("unsupported out_dtype %s" % out_dtype)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, causal, scale, _TORCH_TO_ATTN[q.dtype],
+                      _TORCH_TO_ATTN[out_dtype], stream)
+    if st != 0:
+        msg = status_string(st)
+        if st == 5:
+            msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
+        raise AttnError(st, msg)
+    return out, lse

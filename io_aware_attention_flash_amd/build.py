@@ -1,0 +1,49 @@
+"""Build libattn_fwd.so (the gfx950 HIP kernels and the C ABI) in-tree.
+
+    python -m io_aware_attention_flash_amd.build
+
+hipcc cross-compiles for gfx950 on a machine without a GPU. Packed-fp32
+instructions are disabled for all device code.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+LIB = os.path.join(PKG, "libattn_fwd.so")
+INCLUDE = os.path.join(ROOT, "include")
+ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
+
+HIPCC_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-shared", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose=False, extra=()):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + ["-I", INCLUDE, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building %s" % LIB)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale():
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    srcs = [SRC, os.path.join(INCLUDE, "attn.h")]
+    return any(os.path.getmtime(s) > t for s in srcs)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

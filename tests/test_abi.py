@@ -1,0 +1,105 @@
+"""The C ABI on a host without a GPU: the library loads, exports every
+function include/attn.h declares, agrees with the header's constants, and
+rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from io_aware_attention_flash_amd import binding
+from io_aware_attention_flash_amd import build as hipbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if hipbuild.is_stale():
+        hipbuild.build()
+    return binding.load_library()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def _header_enum(name):
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(%s_[A-Z0-9_]+)\s*=\s*(\d+)" % name, text)}
+
+
+def test_exports_every_declared_function(lib):
+    declared = _header_functions()
+    assert set(declared) == set(binding.EXPORTS)
+    for fn in declared:
+        assert hasattr(lib, fn), "library does not export %s" % fn
+
+
+def test_exported_symbols_are_c_linkage():
+    out = os.popen("nm -D --defined-only %s" % binding.LIB_PATH).read()
+    syms = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for fn in _header_functions():
+        assert fn in syms
+
+
+def test_header_constants_match_binding():
+    st = _header_enum("ATTN_ERR")
+    st["ATTN_OK"] = 0
+    assert {v: k for k, v in st.items()} == binding.STATUS
+    dt = {k: v for k, v in _header_enum("ATTN").items() if k in ("ATTN_F32", "ATTN_F16", "ATTN_BF16")}
+    assert dt == {"ATTN_F32": binding.ATTN_F32, "ATTN_F16": binding.ATTN_F16,
+                  "ATTN_BF16": binding.ATTN_BF16}
+    ver = int(re.search(r"#define ATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert binding.load_library().attn_abi_version() == ver
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        s = binding.status_string(code)
+        assert isinstance(s, str) and s
+    assert binding.status_string(0) == "ok"
+    assert binding.status_string(99) == "unknown status"
+    assert lib.attn_last_hip_error() == 0
+
+
+# Fake, never-dereferenced addresses: validation fails before any use.
+P = 0x1000
+
+
+@pytest.mark.parametrize("args,code", [
+    # null pointers
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    # shapes
+    (dict(B=0), 2), (dict(H=0), 2), (dict(N=0), 2), (dict(N=-5), 2),
+    (dict(N=(1 << 24) + 1), 2), (dict(B=1 << 12, H=(1 << 12) + 1), 2),
+    # head dims and dtype pairs
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=0), 3), (dict(d=256), 3),
+    (dict(i=0, o_t=1), 3), (dict(i=0, o_t=2), 3), (dict(i=1, o_t=2), 3),
+    (dict(i=2, o_t=1), 3), (dict(i=3, o_t=3), 3), (dict(i=2, o_t=7), 3),
+    # scale
+    (dict(scale=float("nan")), 4), (dict(scale=float("inf")), 4),
+    (dict(scale=float("-inf")), 4), (dict(scale=-0.125), 4),
+])
+def test_error_paths_need_no_gpu(lib, args, code):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=128, d=64, causal=0, scale=0.125,
+             i=2, o_t=2)
+    a.update(args)
+    st = binding.attn_fwd_raw(a["q"] or None, a["k"] or None, a["v"] or None, a["o"] or None,
+                              a["lse"] or None, a["B"], a["H"], a["N"], a["d"], a["causal"],
+                              a["scale"], a["i"], a["o_t"])
+    assert st == code, (args, st)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load_library(str(tmp_path / "nope.so"))
+
+
+def test_package_import_loads_nothing():
+    import io_aware_attention_flash_amd as pkg
+    assert callable(pkg.attn_fwd)
+    assert ctypes is not None
