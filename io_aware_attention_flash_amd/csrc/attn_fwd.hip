@@ -46,6 +46,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// fp32 kernel shape (the bf16/fp16 kernel defines its own below).
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBlockM = 128;  // query rows per workgroup (32 per wave)
@@ -58,27 +59,22 @@ struct FwdParams {
   float *lse;
   int N;         // sequence length
   int nq;        // query tiles per (batch, head)
+  int BH;        // batch * heads
   float qk;      // scale * log2(e), >= FLT_MIN
 };
 
-// Workgroups are handed to the 8 XCDs round-robin by linear id. Remap the id
-// so that each XCD receives one contiguous range of work items: all query
-// tiles of a (batch, head) then run on one XCD and share its L2 for K/V.
-__device__ __forceinline__ int xcd_remap(int w, int G) {
-  const int q = G >> 3, r = G & 7;
-  const int x = w & 7, local = w >> 3;
-  const int base = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-  return base + local;
-}
-
-// Work item -> (bh, query tile). Causal tiles are issued longest first
-// within each (batch, head).
+// Work item of this workgroup: (bh, query tile). Workgroups are dispatched
+// in id order and handed to the 8 XCDs round-robin, so id w runs on XCD
+// w % 8. Ids are enumerated tile-major, head-minor: causal tiles go longest
+// first across all heads (greedy longest-first keeps the tail short), and
+// when B*H is a multiple of 8 every tile of head bh runs on XCD bh % 8,
+// where its K/V stay in that XCD's L2.
 template <bool CAUSAL>
 __device__ __forceinline__ void work_item(const FwdParams &p, int &bh, int &qt) {
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  bh = item / p.nq;
-  qt = item - bh * p.nq;
-  if (CAUSAL) qt = p.nq - 1 - qt;
+  const int w = blockIdx.x;
+  const int t = w / p.BH;
+  bh = w - t * p.BH;
+  qt = CAUSAL ? p.nq - 1 - t : t;
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -98,6 +94,8 @@ __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32);
 // --------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // --------------------------------------------------------------------------
+constexpr int kThreads16 = kThreads;  // 4 waves, 128 query rows per workgroup
+constexpr int kBlockM16 = kBlockM;
 // Tile shapes: D=128 uses BN=64 keys per tile, D=64 uses BN=128, so that one
 // thread moves exactly one 4-key x 8-column unit of V per tile.
 template <int D>
@@ -107,28 +105,33 @@ struct Shape16 {
   static constexpr int VSTR = BN + 8;  // V^T row stride in LDS (elements), 16 B pad
   static constexpr int K_ELEMS = BN * KSTR;
   static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;  // one buffer, uint16 elements
   static constexpr int K_CHUNKS = BN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static_assert((BN / 4) * (D / 8) == kThreads, "one V unit per thread");
+  static constexpr int KG = BN / 4;                        // 4-key groups per tile
+  static constexpr int NKB = BN / 32;                      // 32-key blocks per tile
+  static constexpr int NCB = D / 32;                       // 32-column blocks of O^T
+  static constexpr int NKC = D / 16;                       // 16-wide QK^T k-chunks
+  static constexpr int NT = BN / 16;                       // 16-key PV k-chunks
+  static_assert(KG * (D / 8) == kThreads, "one V unit per thread");
   static_assert(K_CHUNKS * kThreads * 8 == BN * D, "K chunks cover the tile");
 };
 
-// Position of key `kl` (0..BN-1 within the tile) in a V^T row. Keys
+// Rows of the online softmax are rescaled only when their maximum grows by
+// more than this many powers of two; otherwise exponentials are taken
+// against the stale maximum and stay <= 2^8, which fp16 P and the fp32
+// accumulators hold exactly as well. The final O / l and LSE use the same
+// reference, so the result is the same in exact arithmetic.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Position of key 4*kg (within the tile) in a V^T row. Keys
 // 16t + 8h + 4g + q (h, g in {0,1}, q in 0..3) go to 16t + 8g + 4h + q, so the
 // eight keys lane group g feeds to the t-th P.V instruction are contiguous.
-__device__ __forceinline__ int vt_pos4(int kg) {  // kg = key / 4
+__device__ __forceinline__ int vt_pos4(int kg) {
   return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
 }
 
-template <int D, bool IS_BF16>
-struct TileRegs16 {
-  u32x4 k[Shape16<D>::K_CHUNKS];
-  u32x4 v[4];
-};
-
-template <int D, bool IS_BF16>
-__device__ __forceinline__ void load_tile16(TileRegs16<D, IS_BF16> &r, const uint16_t *Kh,
-                                            const uint16_t *Vh, int n0, int N, int tid) {
+// Global -> registers for the K tile starting at key n0 (keys >= N read 0).
+template <int D>
+__device__ __forceinline__ void load_k16(u32x4 *rk, const uint16_t *Kh, int n0, int N, int tid) {
   using S = Shape16<D>;
   constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
@@ -136,51 +139,70 @@ __device__ __forceinline__ void load_tile16(TileRegs16<D, IS_BF16> &r, const uin
     const int chunk = tid + c * kThreads;
     const int row = chunk / CPR, col8 = chunk % CPR;
     const int key = n0 + row;
-    r.k[c] = key < N ? *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + col8 * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
-  }
-  const int cg = tid % CPR, kg = tid / CPR;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int key = n0 + kg * 4 + q;
-    r.v[q] = key < N ? *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + cg * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+    rk[c] = key < N ? *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + col8 * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
   }
 }
 
-template <int D, bool IS_BF16>
-__device__ __forceinline__ void store_tile16(const TileRegs16<D, IS_BF16> &r, uint16_t *stage,
-                                             int tid) {
+// Global -> registers for the V tile at n0: thread (kg = tid % KG,
+// cg = tid / KG) holds keys 4kg..4kg+3 of columns 8cg..8cg+7, so the lanes
+// sharing cg later write one V^T row together.
+template <int D>
+__device__ __forceinline__ void load_v16(u32x4 *rv, const uint16_t *Vh, int n0, int N, int tid) {
+  using S = Shape16<D>;
+  const int kg = tid % S::KG, cg = tid / S::KG;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int key = n0 + kg * 4 + q;
+    rv[q] = key < N ? *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + cg * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Registers -> K stage: chunk c of this thread (row-major, padded rows).
+template <int D>
+__device__ __forceinline__ void store_k16_chunk(const u32x4 *rk, uint16_t *lk, int tid, int c) {
   using S = Shape16<D>;
   constexpr int CPR = D / 8;
-  uint16_t *lk = stage;
-  uint16_t *lv = stage + S::K_ELEMS;
+  const int chunk = tid + c * kThreads;
+  const int row = chunk / CPR, col8 = chunk % CPR;
+  *reinterpret_cast<u32x4 *>(lk + row * S::KSTR + col8 * 8) = rk[c];
+}
+
+template <int D>
+__device__ __forceinline__ void store_k16(const u32x4 *rk, uint16_t *lk, int tid) {
 #pragma unroll
-  for (int c = 0; c < S::K_CHUNKS; ++c) {
-    const int chunk = tid + c * kThreads;
-    const int row = chunk / CPR, col8 = chunk % CPR;
-    *reinterpret_cast<u32x4 *>(lk + row * S::KSTR + col8 * 8) = r.k[c];
-  }
-  // V unit: keys 4kg..4kg+3, columns 8cg..8cg+7 -> V^T rows 8cg+e, 4 keys each.
-  const int cg = tid % CPR, kg = tid / CPR;
+  for (int c = 0; c < Shape16<D>::K_CHUNKS; ++c) store_k16_chunk<D>(rk, lk, tid, c);
+}
+
+// V unit -> V^T (fp16), part w of 4: columns 8cg+2w and 8cg+2w+1, four keys
+// each. Lanes with equal cg fill one V^T row, so the writes are free of bank
+// conflicts.
+template <int D, bool IS_BF16>
+__device__ __forceinline__ void store_v16_part(const u32x4 *rv, uint16_t *lv, int tid, int w) {
+  using S = Shape16<D>;
+  const int kg = tid % S::KG, cg = tid / S::KG;
   uint16_t *dst = lv + (cg * 8) * S::VSTR + vt_pos4(kg);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {  // dword w holds columns 2w, 2w+1
-    uint32_t lo0, lo1, hi0, hi1;   // (keys 0,1) and (keys 2,3) for columns 2w and 2w+1
-    if (IS_BF16) {
-      lo0 = pack_f16(bf16_lo_to_f32(r.v[0][w]), bf16_lo_to_f32(r.v[1][w]));
-      hi0 = pack_f16(bf16_lo_to_f32(r.v[2][w]), bf16_lo_to_f32(r.v[3][w]));
-      lo1 = pack_f16(bf16_hi_to_f32(r.v[0][w]), bf16_hi_to_f32(r.v[1][w]));
-      hi1 = pack_f16(bf16_hi_to_f32(r.v[2][w]), bf16_hi_to_f32(r.v[3][w]));
-    } else {
-      lo0 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x05040100u);
-      hi0 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x05040100u);
-      lo1 = __builtin_amdgcn_perm(r.v[1][w], r.v[0][w], 0x07060302u);
-      hi1 = __builtin_amdgcn_perm(r.v[3][w], r.v[2][w], 0x07060302u);
-    }
-    *reinterpret_cast<u32x2 *>(dst + (2 * w) * S::VSTR) = u32x2{lo0, hi0};
-    *reinterpret_cast<u32x2 *>(dst + (2 * w + 1) * S::VSTR) = u32x2{lo1, hi1};
+  uint32_t lo0, lo1, hi0, hi1;  // (keys 0,1) and (keys 2,3) for columns 2w and 2w+1
+  if (IS_BF16) {
+    lo0 = pack_f16(bf16_lo_to_f32(rv[0][w]), bf16_lo_to_f32(rv[1][w]));
+    hi0 = pack_f16(bf16_lo_to_f32(rv[2][w]), bf16_lo_to_f32(rv[3][w]));
+    lo1 = pack_f16(bf16_hi_to_f32(rv[0][w]), bf16_hi_to_f32(rv[1][w]));
+    hi1 = pack_f16(bf16_hi_to_f32(rv[2][w]), bf16_hi_to_f32(rv[3][w]));
+  } else {
+    lo0 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);
+    hi0 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x05040100u);
+    lo1 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x07060302u);
+    hi1 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x07060302u);
   }
+  *reinterpret_cast<u32x2 *>(dst + (2 * w) * S::VSTR) = u32x2{lo0, hi0};
+  *reinterpret_cast<u32x2 *>(dst + (2 * w + 1) * S::VSTR) = u32x2{lo1, hi1};
+}
+
+template <int D, bool IS_BF16>
+__device__ __forceinline__ void store_v16(const u32x4 *rv, uint16_t *lv, int tid) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) store_v16_part<D, IS_BF16>(rv, lv, tid, w);
 }
 
 template <bool IS_BF16>
@@ -198,15 +220,213 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// S^T[kb] = K_kb Q^T for one tile: lane holds its query row and keys
+// 32kb + 8(r/4) + 4g + r%4 of the tile. The two 32-key blocks are
+// independent accumulation chains and are interleaved.
+template <int D, bool IS_BF16>
+__device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *lk, int l32,
+                                        int g) {
+  using S = Shape16<D>;
+#pragma unroll
+  for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < S::NKC; ++kc)
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb) {
+      const u32x4 a =
+          *reinterpret_cast<const u32x4 *>(lk + (kb * 32 + l32) * S::KSTR + kc * 16 + g * 8);
+      s[kb] = mfma_qk<IS_BF16>(a, qf[kc], s[kb]);
+    }
+}
+
+// Per-lane online-softmax state: one query row, half of each tile's keys.
+template <int D>
+struct RowState16 {
+  f32x16 acc[D / 32];  // O^T columns of this row (unnormalised)
+  float m;             // reference maximum, base-2 units; -inf before any key
+  float neg_m;         // -m, or 0 while m = -inf
+  float l;             // sum of this lane's rounded weights
+};
+
+// Online-softmax update for one tile of scores, first half: mask (boundary
+// tiles only), row maximum, lazy rescale of the state.
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0, int N, int qrow,
+                                            float qk, int g) {
+  using S = Shape16<D>;
+  if constexpr (MASK) {  // key tail and/or causal diagonal: hidden keys get -inf
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        const bool dead = key >= N || (CAUSAL && key > qrow);
+        s[kb][r] = dead ? -INFINITY : s[kb][r];
+      }
+  }
+  // Row maximum of the scaled scores (qk > 0, so it is max(s) * qk).
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+  mx = fmaxf(mx, shfl_xor32(mx));
+  const float m_tile = mx * qk;
+  if (__any(m_tile > st.m + kRescaleLog2)) {  // wave-uniform: some row grew a lot
+    const float m_new = fmaxf(st.m, m_tile);
+    const float neg_new = m_new == -INFINITY ? 0.f : -m_new;
+    const float alpha = exp2_fast(st.m + neg_new);  // 0 when m was -inf
+#pragma unroll
+    for (int cb = 0; cb < S::NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.acc[cb][r] *= alpha;
+    st.l *= alpha;
+    st.m = m_new;
+    st.neg_m = neg_new;
+  }
+}
+
+// One packed P^T dword: weights p = 2^(s*qk - m) of two consecutive score
+// registers rounded to fp16, and their (rounded) sum added to *lsum.
+__device__ __forceinline__ uint32_t exp_pair(float s0, float s1, float qk, float neg_m,
+                                             float *lsum) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const float p0 = exp2_fast(fmaf(s0, qk, neg_m));
+  const float p1 = exp2_fast(fmaf(s1, qk, neg_m));
+  const uint32_t h = pack_f16(p0, p1);
+  *lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, *lsum, false);
+  return h;
+}
+
+// Everything one workgroup iteration touches.
+template <int D>
+struct Pipe16 {
+  uint16_t *lds;      // K stage s at lds + s*K_ELEMS, V^T stages after both K stages
+  const uint16_t *Kh, *Vh;
+  u32x4 rk[Shape16<D>::K_CHUNKS];  // K tile j+2 in flight
+  u32x4 rv[4];                     // V tile j+1 in flight
+  f32x16 s[Shape16<D>::NKB];       // scores of the tile being normalised
+  int N, n_tiles, qrow, tid, l32, g;
+  float qk;
+};
+
+// LDS reads run this many MFMA steps ahead of their use.
+constexpr int kLookahead = 3;
+
+// Iteration j of the software pipeline. On entry: K_{j+1} and V_j are in
+// LDS, S_j is in registers.
+//  phase 0: row maxima of S_j and the (rare) rescale of the state;
+//  phase 1: QK^T of tile j+1 on the matrix cores, one MFMA per step, each
+//           step also computing two weights of tile j on the vector ALUs;
+//  phase 2: P_j V_j, one MFMA per step, the first steps also writing the
+//           prefetched V_{j+1} / K_{j+2} into the LDS stages freed last
+//           iteration.
+// Within a phase the vector work of a step does not depend on the MFMA in
+// flight, so the two units run concurrently; scheduling barriers keep the
+// compiler from regrouping the steps. NEXT = false for the last tile.
+template <int D, bool IS_BF16, bool CAUSAL, bool MASK, bool NEXT>
+__device__ __forceinline__ void pipe_iter(Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf, int j) {
+  using S = Shape16<D>;
+  constexpr int BN = S::BN;
+  constexpr int LA = kLookahead;
+  const bool k_next2 = NEXT && j + 2 < pp.n_tiles;
+  const int l32 = pp.l32, g = pp.g;
+  // Stage offsets are selected as integers so the pointers stay in LDS.
+  uint16_t *const k_this = pp.lds + (j & 1) * S::K_ELEMS;
+  uint16_t *const k_next = pp.lds + ((j + 1) & 1) * S::K_ELEMS;
+  uint16_t *const v_this = pp.lds + 2 * S::K_ELEMS + (j & 1) * S::V_ELEMS;
+  uint16_t *const v_next = pp.lds + 2 * S::K_ELEMS + ((j + 1) & 1) * S::V_ELEMS;
+  if (NEXT) {
+    if (k_next2) load_k16<D>(pp.rk, pp.Kh, (j + 2) * BN, pp.N, pp.tid);
+    load_v16<D>(pp.rv, pp.Vh, (j + 1) * BN, pp.N, pp.tid);
+  }
+
+  // ---- phase 0
+  softmax_max<D, CAUSAL, MASK>(st, pp.s, j * BN, pp.N, pp.qrow, pp.qk, g);
+
+  // ---- phase 1: MFMA step i accumulates s_next[kb] += K_kb,kc Q_kc^T with
+  // kc = i / NKB, kb = i % NKB (alternating accumulators), and packs the
+  // next PPS P^T dwords of tile j.
+  constexpr int NM1 = S::NKB * S::NKC;
+  constexpr int PPS = S::NT * 4 / NM1;  // P^T dwords per step (1 for d=128, 2 for d=64)
+  static_assert(PPS * NM1 == S::NT * 4, "P^T dwords split evenly over the QK^T MFMAs");
+  f32x16 s_next[S::NKB];
+  u32x4 pf[S::NT];
+  float lsum = 0.f;
+  const float qk = pp.qk, neg_m = st.neg_m;
+  u32x4 kf[LA + 1];
+  const uint16_t *kbase = k_next + l32 * S::KSTR + g * 8;
+  if (NEXT) {
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < LA; ++i)
+      kf[i] = *reinterpret_cast<const u32x4 *>(kbase + (i % S::NKB) * 32 * S::KSTR +
+                                               (i / S::NKB) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NM1; ++i) {
+    if (NEXT) {
+      const int ia = i + LA;
+      if (ia < NM1)
+        kf[ia % (LA + 1)] = *reinterpret_cast<const u32x4 *>(
+            kbase + (ia % S::NKB) * 32 * S::KSTR + (ia / S::NKB) * 16);
+      const int kb = i % S::NKB, kc = i / S::NKB;
+      s_next[kb] = mfma_qk<IS_BF16>(kf[i % (LA + 1)], qf[kc], s_next[kb]);
+    }
+#pragma unroll
+    for (int q = 0; q < PPS; ++q) {
+      const int dw = i * PPS + q, t = dw >> 2, w = dw & 3;
+      const int kb = t >> 1, r = 8 * (t & 1) + 2 * w;
+      pf[t][w] = exp_pair(pp.s[kb][r], pp.s[kb][r + 1], qk, neg_m, &lsum);
+      asm volatile("" ::"v"(pf[t][w]));  // keep this step's weights in this step
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  st.l += lsum;
+
+  // ---- phase 2: MFMA step i accumulates acc[cb] += V^T_cb,t P^T_t with
+  // t = i / NCB, cb = i % NCB.
+  constexpr int NM2 = S::NT * S::NCB;
+  u32x4 vf[LA + 1];
+  const uint16_t *vbase = v_this + l32 * S::VSTR + 8 * g;
+#pragma unroll
+  for (int i = 0; i < LA; ++i)
+    vf[i] = *reinterpret_cast<const u32x4 *>(vbase + (i % S::NCB) * 32 * S::VSTR +
+                                             16 * (i / S::NCB));
+#pragma unroll
+  for (int i = 0; i < NM2; ++i) {
+    const int ia = i + LA;
+    if (ia < NM2)
+      vf[ia % (LA + 1)] = *reinterpret_cast<const u32x4 *>(
+          vbase + (ia % S::NCB) * 32 * S::VSTR + 16 * (ia / S::NCB));
+    const int cb = i % S::NCB, t = i / S::NCB;
+    st.acc[cb] = mfma_pv(vf[i % (LA + 1)], pf[t], st.acc[cb]);
+    if (NEXT) {
+      if (i < 4) store_v16_part<D, IS_BF16>(pp.rv, v_next, pp.tid, i);
+      if (i >= 4 && i < 4 + S::K_CHUNKS && k_next2)
+        store_k16_chunk<D>(pp.rk, k_this, pp.tid, i - 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (NEXT) {
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb) pp.s[kb] = s_next[kb];
+    __syncthreads();
+  }
+}
+
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
-  constexpr int NKB = BN / 32;  // 32-key blocks per tile
-  constexpr int NCB = D / 32;   // 32-column blocks of O^T
-  constexpr int NKC = D / 16;   // 16-wide k-chunks of the QK^T contraction
-  constexpr int NT = BN / 16;   // 16-key chunks of the PV contraction
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::STAGE];
+  constexpr int NCB = S::NCB;
+  constexpr int NKC = S::NKC;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::K_ELEMS + 2 * S::V_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -218,16 +438,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
   const int m0 = qt * kBlockM;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + head;
-  const uint16_t *Kh = static_cast<const uint16_t *>(p.k) + head;
-  const uint16_t *Vh = static_cast<const uint16_t *>(p.v) + head;
 
+  Pipe16<D> pp;
+  pp.lds = lds;
+  pp.Kh = static_cast<const uint16_t *>(p.k) + head;
+  pp.Vh = static_cast<const uint16_t *>(p.v) + head;
+  pp.N = N;
+  pp.tid = tid;
+  pp.l32 = l32;
+  pp.g = g;
+  pp.qk = p.qk;
   // This lane's query row; rows past N read as zero and are never stored.
-  const int qrow = m0 + wave * 32 + l32;
+  pp.qrow = m0 + wave * 32 + l32;
+
   u32x4 qf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc)
-    qf[kc] = qrow < N ? *reinterpret_cast<const u32x4 *>(Qh + (size_t)qrow * D + kc * 16 + g * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
+    qf[kc] = pp.qrow < N
+                 ? *reinterpret_cast<const u32x4 *>(Qh + (size_t)pp.qrow * D + kc * 16 + g * 8)
+                 : u32x4{0u, 0u, 0u, 0u};
 
   // KV tiles to visit. Causal: only tiles holding some key <= the block's
   // last row. Tiles [0, n_full) need no mask at all.
@@ -235,116 +464,53 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
   const int n_tiles = CAUSAL ? min(n_all, (m0 + kBlockM + BN - 1) / BN) : n_all;
   int n_full = N / BN;
   if (CAUSAL) n_full = min(n_full, (m0 + 1) / BN);
+  pp.n_tiles = n_tiles;
 
-  f32x16 acc[NCB];
+  RowState16<D> st;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[cb][r] = 0.f;
-  float m_i = -INFINITY;  // running max, base-2 units (scores * qk)
-  float l_i = 0.f;        // running sum over this lane's half of the keys
-  const float qk = p.qk;
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    for (int r = 0; r < 16; ++r) st.acc[cb][r] = 0.f;
+  st.m = -INFINITY;
+  st.neg_m = 0.f;
+  st.l = 0.f;
 
-  TileRegs16<D, IS_BF16> tr;
-  load_tile16<D, IS_BF16>(tr, Kh, Vh, 0, N, tid);
-  store_tile16<D, IS_BF16>(tr, lds, tid);
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const uint16_t *lk = lds + (j & 1) * S::STAGE;
-    const uint16_t *lv = lk + S::K_ELEMS;
-    const int n0 = j * BN;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) load_tile16<D, IS_BF16>(tr, Kh, Vh, n0 + BN, N, tid);
-
-    // S^T[kb] = K_kb Q^T : lane holds query qrow, keys n0 + 32kb + 8(r/4) + 4g + r%4.
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4 *>(lk + (kb * 32 + l32) * S::KSTR + kc * 16 + g * 8);
-        s[kb] = mfma_qk<IS_BF16>(a, qf[kc], s[kb]);
-      }
-    }
-
-    if (j >= n_full) {  // boundary tile: key tail and/or causal diagonal
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool dead = key >= N || (CAUSAL && key > qrow);
-          s[kb][r] = dead ? -INFINITY : s[kb][r];
-        }
-    }
-
-    // Online softmax update for this lane's row (qk > 0, so max(s)*qk is the
-    // max of the scaled scores; masked entries stay -inf).
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, shfl_xor32(mx));
-    const float m_new = fmaxf(m_i, mx * qk);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all-masked guard
-    const float alpha = exp2_fast(m_i - m_use);
-    const float neg_m = -m_use;
-
-    u32x4 pf[NT];  // P^T operands, fp16
-    float lsum = 0.f;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int kb = t >> 1, r0 = 8 * (t & 1);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float p0 = exp2_fast(fmaf(s[kb][r0 + 2 * w], qk, neg_m));
-        const float p1 = exp2_fast(fmaf(s[kb][r0 + 2 * w + 1], qk, neg_m));
-        const uint32_t h = pack_f16(p0, p1);
-        pf[t][w] = h;
-        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, lsum, false);
-      }
-    }
-    l_i = l_i * alpha + lsum;
-    m_i = m_new;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[cb][r] *= alpha;
-
-    // O^T[cb] += V^T[cb] P^T
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4 *>(lv + (cb * 32 + l32) * S::VSTR + 16 * t + 8 * g);
-        acc[cb] = mfma_pv(a, pf[t], acc[cb]);
-      }
-
-    if (has_next) store_tile16<D, IS_BF16>(tr, lds + ((j + 1) & 1) * S::STAGE, tid);
-    __syncthreads();
+  // Prologue: K_0, V_0 and K_1 into LDS, then S_0.
+  load_k16<D>(pp.rk, pp.Kh, 0, N, tid);
+  load_v16<D>(pp.rv, pp.Vh, 0, N, tid);
+  store_k16<D>(pp.rk, lds, tid);
+  store_v16<D, IS_BF16>(pp.rv, lds + 2 * S::K_ELEMS, tid);
+  if (n_tiles > 1) {
+    load_k16<D>(pp.rk, pp.Kh, BN, N, tid);
+    store_k16<D>(pp.rk, lds + S::K_ELEMS, tid);
   }
+  __syncthreads();
+  qk_tile<D, IS_BF16>(pp.s, qf, lds, l32, g);
+
+  int j = 0;
+  const int n_pipe = min(n_full, n_tiles - 1);  // unmasked tiles with a successor
+  for (; j < n_pipe; ++j) pipe_iter<D, IS_BF16, CAUSAL, false, true>(pp, st, qf, j);
+  for (; j < n_tiles - 1; ++j) pipe_iter<D, IS_BF16, CAUSAL, true, true>(pp, st, qf, j);
+  if (j < n_full)
+    pipe_iter<D, IS_BF16, CAUSAL, false, false>(pp, st, qf, j);
+  else
+    pipe_iter<D, IS_BF16, CAUSAL, true, false>(pp, st, qf, j);
 
   // Epilogue: combine the two key halves of the row sum, divide once, LSE.
-  const float l_tot = l_i + shfl_xor32(l_i);
+  const float l_tot = st.l + shfl_xor32(st.l);
   const float l_safe = l_tot > 0.f ? l_tot : 1.f;
   const float inv = 1.0f / l_safe;
+  const int qrow = pp.qrow;
   if (qrow < N) {
-    if (g == 0) p.lse[(size_t)bh * N + qrow] = (m_i + log2_fast(l_safe)) * 0.69314718055994531f;
+    if (g == 0) p.lse[(size_t)bh * N + qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
     const size_t orow = head + (size_t)qrow * D;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         const int c0 = cb * 32 + r4 * 8 + g * 4;
-        const float o0 = acc[cb][4 * r4 + 0] * inv, o1 = acc[cb][4 * r4 + 1] * inv;
-        const float o2 = acc[cb][4 * r4 + 2] * inv, o3 = acc[cb][4 * r4 + 3] * inv;
+        const float o0 = st.acc[cb][4 * r4 + 0] * inv, o1 = st.acc[cb][4 * r4 + 1] * inv;
+        const float o2 = st.acc[cb][4 * r4 + 2] * inv, o3 = st.acc[cb][4 * r4 + 3] * inv;
         if (OUT_F32) {
           *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + orow + c0) = f32x4{o0, o1, o2, o3};
         } else if (IS_BF16) {
@@ -530,7 +696,11 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
   if (in_dtype != ATTN_F32 && out_dtype != in_dtype && out_dtype != ATTN_F32)
     return ATTN_ERR_UNSUPPORTED;
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  const int64_t nq = (N + kBlockM - 1) / kBlockM;
+  // Query rows per workgroup and threads per workgroup of the chosen kernel.
+  const bool f32_path = in_dtype == ATTN_F32;
+  const int64_t block_m = f32_path ? kBlockM : kBlockM16;
+  const unsigned threads = f32_path ? kThreads : kThreads16;
+  const int64_t nq = (N + block_m - 1) / block_m;
   const int64_t grid = nq * B * H;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
 
@@ -542,6 +712,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
   p.lse = lse;
   p.N = (int)N;
   p.nq = (int)nq;
+  p.BH = (int)(B * H);
   // scale * log2(e) in double, rounded once; a zero scale becomes FLT_MIN so
   // masked scores (-inf) never meet a 0 factor.
   double qk = (double)scale * 1.4426950408889634;
@@ -552,7 +723,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                         : pick_d<128>(in_dtype, out_f32, causal != 0);
   void *args[] = {&p};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
-                                         dim3(kThreads), args, 0, (hipStream_t)stream);
+                                         dim3(threads), args, 0, (hipStream_t)stream);
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return ATTN_ERR_HIP;

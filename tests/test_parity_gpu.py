@@ -196,14 +196,16 @@ def test_deterministic_bitwise():
 @pytest.mark.parametrize("dt", ["bf16", "f16", "f32"])
 def test_head_dim_zero_padding(dt):
     """d=64 data zero-padded to d=128 at the same scale: same O and LSE
-    (exact in the math; equal here up to accumulation order)."""
+    (exact in the math). The two head dims run with different key-tile
+    widths, so p is rounded to fp16 against different running maxima and the
+    results agree to the parity tolerance, not bitwise."""
     q, k, v = make_qkv(1, 2, 257, 64, dt, 1.0, seed=8)
     pad = lambda x: torch.cat([x, torch.zeros_like(x)], dim=-1)  # noqa: E731
     o64, l64 = gpu_attn(q, k, v, True, 0.125)
     o128, l128 = gpu_attn(pad(q), pad(k), pad(v), True, 0.125)
     assert float(o128[..., 64:].abs().max()) == 0.0
     assert float((o128[..., :64] - o64).abs().max()) <= 2e-3
-    assert float((l128 - l64).abs().max()) <= 1e-4
+    assert float((l128 - l64).abs().max()) <= LSE_MAX
 
 
 def test_out_and_lse_buffers_untouched_outside():
