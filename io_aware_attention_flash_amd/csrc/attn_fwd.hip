@@ -22,17 +22,20 @@
 //    straight from the S^T accumulators of the same lane (converted to
 //    fp16), and the O^T accumulator has the same row-per-lane layout, so
 //    rescaling by alpha is a per-lane scalar multiply.
-//  * K tiles are staged in LDS as they are in memory (row-major, 16-byte
-//    padded rows); V tiles are written to LDS transposed (V^T, key-permuted
-//    so each lane's eight keys are contiguous) and, for bf16 inputs,
-//    converted to fp16 on the way. Both are double-buffered: the global
-//    loads of tile j+1 are in flight while tile j is computed.
+//  * K and V tiles are copied from memory straight into LDS rings
+//    (buffer_load ... lds) and read from there by all four waves: K as the
+//    A operand of QK^T, V through transposing reads (ds_read_b64_tr_b16)
+//    as the A operand of O^T. bf16 V is converted to fp16 in place in LDS.
+//  * each iteration is one stream of MFMAs (QK^T of the next tile, then P.V
+//    of this one) with the softmax work spread across it: on gfx950 a
+//    wave's vector instructions overlap its own MFMAs, not another wave's.
 //  * fp32 inputs use a separate kernel on v_mfma_f32_32x32x2_f32.
 #include <hip/hip_runtime.h>
 
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+
 
 #include "attn.h"
 
@@ -91,28 +94,60 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
 
 __device__ __forceinline__ float shfl_xor32(float x) { return __shfl_xor(x, 32); }
 
+// max / sum of x over lanes l and l ^ 32, without an LDS round trip:
+// v_permlane32_swap exchanges the upper half of one register with the lower
+// half of another, so swapping x with itself leaves {x[l], x[l ^ 32]} in the
+// two results of every lane.
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // --------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // --------------------------------------------------------------------------
-constexpr int kThreads16 = kThreads;  // 4 waves, 128 query rows per workgroup
-constexpr int kBlockM16 = kBlockM;
-// Tile shapes: D=128 uses BN=64 keys per tile, D=64 uses BN=128, so that one
-// thread moves exactly one 4-key x 8-column unit of V per tile.
+// A workgroup is 4 wave64s and 128 query rows (32 per wave); two
+// workgroups share a CU, so the two waves on a SIMD never wait on each
+// other. K and V tiles go from global memory straight into LDS
+// (buffer_load ... lds, no register staging): K through a ring of three
+// stages (fetched two iterations before use), V through two (one iteration
+// before). Both stay row-major; 16-byte chunks are XOR-swizzled per row so
+// the lane-contiguous DMA writes, the K operand reads and the transposing V
+// reads (ds_read_b64_tr_b16) are free of bank conflicts or nearly so. bf16 V
+// is converted to fp16 in place in LDS (the P.V product runs in fp16, see
+// the header), each thread converting the 64 bytes its own copy brought in.
+// Tiles: d=128 uses 64 keys, d=64 uses 128.
+//
+// On gfx950 a wave's vector instructions run in the shadow of its own MFMAs,
+// not of another wave's, so each iteration is one stream of 2 x 16 MFMAs
+// (QK^T of tile j+1, then P_j V_j) with the softmax work of the tile -- the
+// exponentials of S_j and the row maximum of S_{j+1} -- spread over all of
+// its steps.
+constexpr int kWaves16 = 4;
+constexpr int kThreads16 = kWaves16 * 64;
+constexpr int kBlockM16 = kWaves16 * 32;
+constexpr int kKStages = 3;
+constexpr int kVStages = 2;
+
 template <int D>
 struct Shape16 {
   static constexpr int BN = (D == 128) ? 64 : 128;
-  static constexpr int KSTR = D + 8;   // K row stride in LDS (elements), 16 B pad
-  static constexpr int VSTR = BN + 8;  // V^T row stride in LDS (elements), 16 B pad
-  static constexpr int K_ELEMS = BN * KSTR;
-  static constexpr int V_ELEMS = D * VSTR;
-  static constexpr int K_CHUNKS = BN * D / 8 / kThreads;  // 16-byte K chunks per thread
-  static constexpr int KG = BN / 4;                        // 4-key groups per tile
-  static constexpr int NKB = BN / 32;                      // 32-key blocks per tile
-  static constexpr int NCB = D / 32;                       // 32-column blocks of O^T
-  static constexpr int NKC = D / 16;                       // 16-wide QK^T k-chunks
-  static constexpr int NT = BN / 16;                       // 16-key PV k-chunks
-  static_assert(KG * (D / 8) == kThreads, "one V unit per thread");
-  static_assert(K_CHUNKS * kThreads * 8 == BN * D, "K chunks cover the tile");
+  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
+  static constexpr int TILE_ELEMS = BN * D;              // one K or V stage
+  static constexpr int TILE_BYTES = TILE_ELEMS * 2;
+  static constexpr int DMA_INS = BN * CPR / kThreads16;  // DMA instructions per thread and tile
+  static constexpr int NKB = BN / 32;                    // 32-key blocks per tile
+  static constexpr int NCB = D / 32;                     // 32-column blocks of O^T
+  static constexpr int NKC = D / 16;                     // 16-wide QK^T k-chunks
+  static constexpr int NT = BN / 16;                     // 16-key PV k-chunks
+  static_assert(DMA_INS * kThreads16 == BN * CPR, "DMA covers the tile");
+  static_assert(DMA_INS * kThreads16 * 16 == TILE_BYTES, "each DMA instruction moves 4 KiB");
 };
 
 // Rows of the online softmax are rescaled only when their maximum grows by
@@ -122,87 +157,96 @@ struct Shape16 {
 // reference, so the result is the same in exact arithmetic.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Position of key 4*kg (within the tile) in a V^T row. Keys
-// 16t + 8h + 4g + q (h, g in {0,1}, q in 0..3) go to 16t + 8g + 4h + q, so the
-// eight keys lane group g feeds to the t-th P.V instruction are contiguous.
-__device__ __forceinline__ int vt_pos4(int kg) {
-  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-}
-
-// Global -> registers for the K tile starting at key n0 (keys >= N read 0).
+// Chunk swizzles: chunk x of row r is stored at x ^ swz(r).
+//  K: the 16 rows one K operand read touches (same logical chunk) land on 16
+//     different bank groups.
+//  V: the 4 rows x 4 chunks of one transposing read land on each bank at
+//     most twice.
+// Both only depend on the row modulo 16, so they repeat within the 16 (d=128)
+// or 32 (d=64) rows one DMA instruction covers.
 template <int D>
-__device__ __forceinline__ void load_k16(u32x4 *rk, const uint16_t *Kh, int n0, int N, int tid) {
-  using S = Shape16<D>;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-  for (int c = 0; c < S::K_CHUNKS; ++c) {
-    const int chunk = tid + c * kThreads;
-    const int row = chunk / CPR, col8 = chunk % CPR;
-    const int key = n0 + row;
-    rk[c] = key < N ? *reinterpret_cast<const u32x4 *>(Kh + (size_t)key * D + col8 * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-  }
+__device__ __forceinline__ int swz_k(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
 }
-
-// Global -> registers for the V tile at n0: thread (kg = tid % KG,
-// cg = tid / KG) holds keys 4kg..4kg+3 of columns 8cg..8cg+7, so the lanes
-// sharing cg later write one V^T row together.
 template <int D>
-__device__ __forceinline__ void load_v16(u32x4 *rv, const uint16_t *Vh, int n0, int N, int tid) {
-  using S = Shape16<D>;
-  const int kg = tid % S::KG, cg = tid / S::KG;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int key = n0 + kg * 4 + q;
-    rv[q] = key < N ? *reinterpret_cast<const u32x4 *>(Vh + (size_t)key * D + cg * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-  }
+__device__ __forceinline__ int swz_v(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-// Registers -> K stage: chunk c of this thread (row-major, padded rows).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a __shared__ element.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
+}
+
+// Word 3 of a raw (untyped, stride 0) buffer descriptor on gfx9-family parts.
+constexpr int kBufferFlags = 0x00020000;
+
+// Buffer descriptor (four SGPR words) of tile t (keys t*BN ..) of one
+// head's K or V, cut to the keys that exist (empty for tiles past the last
+// one visited), so reads beyond the cut return zeros and touch no memory.
+// Every input is wave-uniform; readfirstlane says so to the compiler, which
+// keeps the words in scalar registers.
 template <int D>
-__device__ __forceinline__ void store_k16_chunk(const u32x4 *rk, uint16_t *lk, int tid, int c) {
-  using S = Shape16<D>;
-  constexpr int CPR = D / 8;
-  const int chunk = tid + c * kThreads;
-  const int row = chunk / CPR, col8 = chunk % CPR;
-  *reinterpret_cast<u32x4 *>(lk + row * S::KSTR + col8 * 8) = rk[c];
+__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N) {
+  constexpr int BN = Shape16<D>::BN;
+  const int keys = t < n_tiles ? min(N - t * BN, BN) : 0;
+  const uint16_t *base = keys > 0 ? head + (size_t)t * BN * D : head;
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,  // stride 0
+               (uint32_t)__builtin_amdgcn_readfirstlane(keys * D * 2), (uint32_t)kBufferFlags};
 }
 
+// One buffer_load_dwordx4 ... lds: 16 bytes per lane from the descriptor at
+// the lane's offset into LDS at lds_byte + 16 * lane. Written as inline
+// assembly on purpose: the compiler then does not treat the copies in flight
+// as possible writers of every LDS location, which would make it wait for
+// all of them before each LDS read; this kernel orders them itself (an
+// explicit vmcnt wait and a barrier before a stage is read, a barrier before
+// it is refilled). M0 carries the LDS address; nothing else here uses it.
+__device__ __forceinline__ void dma16_to_lds(u32x4 rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// DMA of one K or V tile into an LDS stage. Instruction c fills the 16-byte
+// slots c*256 + tid: slot s holds physical chunk s % CPR of tile row s / CPR,
+// i.e. logical chunk (s % CPR) ^ swz(row). Instruction c covers the c-th
+// 4 KiB of the tile, a whole number of swizzle periods, so its lane offset is
+// that of c = 0 plus 4096 c. The offset stays in a VGPR (the descriptor's
+// range check applies to it, not to an SGPR offset).
+template <int D, bool IS_V>
+__device__ __forceinline__ uint32_t dma_offset(int tid) {
+  constexpr int CPR = Shape16<D>::CPR;
+  const int row0 = tid / CPR;
+  const int swz = IS_V ? swz_v<D>(row0) : swz_k<D>(row0);
+  return row0 * D * 2 + (((tid % CPR) ^ swz) << 4);
+}
+// stage_byte: LDS byte address of the stage plus 1024 * wave (wave-uniform).
 template <int D>
-__device__ __forceinline__ void store_k16(const u32x4 *rk, uint16_t *lk, int tid) {
+__device__ __forceinline__ void dma_tile(u32x4 rsrc, uint32_t stage_byte, uint32_t voff) {
 #pragma unroll
-  for (int c = 0; c < Shape16<D>::K_CHUNKS; ++c) store_k16_chunk<D>(rk, lk, tid, c);
+  for (int c = 0; c < Shape16<D>::DMA_INS; ++c)
+    dma16_to_lds(rsrc, stage_byte + c * 4096, voff + c * 4096);
 }
 
-// V unit -> V^T (fp16), part w of 4: columns 8cg+2w and 8cg+2w+1, four keys
-// each. Lanes with equal cg fill one V^T row, so the writes are free of bank
-// conflicts.
-template <int D, bool IS_BF16>
-__device__ __forceinline__ void store_v16_part(const u32x4 *rv, uint16_t *lv, int tid, int w) {
-  using S = Shape16<D>;
-  const int kg = tid % S::KG, cg = tid / S::KG;
-  uint16_t *dst = lv + (cg * 8) * S::VSTR + vt_pos4(kg);
-  uint32_t lo0, lo1, hi0, hi1;  // (keys 0,1) and (keys 2,3) for columns 2w and 2w+1
-  if (IS_BF16) {
-    lo0 = pack_f16(bf16_lo_to_f32(rv[0][w]), bf16_lo_to_f32(rv[1][w]));
-    hi0 = pack_f16(bf16_lo_to_f32(rv[2][w]), bf16_lo_to_f32(rv[3][w]));
-    lo1 = pack_f16(bf16_hi_to_f32(rv[0][w]), bf16_hi_to_f32(rv[1][w]));
-    hi1 = pack_f16(bf16_hi_to_f32(rv[2][w]), bf16_hi_to_f32(rv[3][w]));
-  } else {
-    lo0 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x05040100u);
-    hi0 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x05040100u);
-    lo1 = __builtin_amdgcn_perm(rv[1][w], rv[0][w], 0x07060302u);
-    hi1 = __builtin_amdgcn_perm(rv[3][w], rv[2][w], 0x07060302u);
-  }
-  *reinterpret_cast<u32x2 *>(dst + (2 * w) * S::VSTR) = u32x2{lo0, hi0};
-  *reinterpret_cast<u32x2 *>(dst + (2 * w + 1) * S::VSTR) = u32x2{lo1, hi1};
+// Wait until at most N vector-memory instructions of this wave are
+// outstanding (they retire in order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, bool IS_BF16>
-__device__ __forceinline__ void store_v16(const u32x4 *rv, uint16_t *lv, int tid) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) store_v16_part<D, IS_BF16>(rv, lv, tid, w);
+// LDS writes of this wave done, then a workgroup barrier. (No memory fence:
+// it would also wait for the copies in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
 }
 
 template <bool IS_BF16>
@@ -220,25 +264,66 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x4 a, u32x4 b, f32x16 c) {
                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-// S^T[kb] = K_kb Q^T for one tile: lane holds its query row and keys
-// 32kb + 8(r/4) + 4g + r%4 of the tile. The two 32-key blocks are
-// independent accumulation chains and are interleaved.
+// Lane-constant parts of the LDS operand addresses (elements).
+template <int D>
+struct LaneAddr {
+  int k_off;          // K operand: row l32
+  int k_swz;          // swz_k of this lane's rows, with g folded in
+  int v_off[D / 32];  // V operand (transposing read), per 32-column block
+};
+
+template <int D>
+__device__ __forceinline__ LaneAddr<D> lane_addr(int lane) {
+  LaneAddr<D> la;
+  const int l32 = lane & 31, g = lane >> 5;
+  la.k_swz = swz_k<D>(l32) ^ g;  // logical chunk 2kc + g = 2kc ^ g
+  la.k_off = l32 * D;
+  // Transposing read, 16-lane block (g, h), source lane s = a + 4m: row
+  // 4g + m (plus multiples of 8 rows), columns 32cb + 16h + 4a .. +3.
+  const int s = lane & 15, h = (lane >> 4) & 1;
+  const int a = s & 3, m = s >> 2;
+  const int row = 4 * g + m;
+  const int sv = swz_v<D>(row);
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb) {
+    const int x = 4 * cb + 2 * h + (a >> 1);
+    la.v_off[cb] = row * D + (x ^ sv) * 8 + (a & 1) * 4;
+  }
+  return la;
+}
+
+// K operand of QK^T step (kb, kc): K[32kb + l32][16kc + 8g .. +7].
+template <int D>
+__device__ __forceinline__ u32x4 k_frag(const uint16_t *kst, const LaneAddr<D> &la, int kb,
+                                        int kc) {
+  return *reinterpret_cast<const u32x4 *>(kst + la.k_off + kb * 32 * D +
+                                          (((2 * kc) ^ la.k_swz) << 3));
+}
+
+// V^T operand of PV step (t, cb): keys 16t + 8u + 4g + 0..3 (u = 0, 1) of
+// column 32cb + l32, as 8 fp16 values -- the key order of the P^T operand
+// taken from the S^T accumulators.
+template <int D>
+__device__ __forceinline__ u32x4 v_frag(const uint16_t *vst, const LaneAddr<D> &la, int t, int cb) {
+  const uint16_t *p0 = vst + la.v_off[cb] + (16 * t) * D;
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p0));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p0 + 8 * D));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+  return u32x4{w0[0], w0[1], w1[0], w1[1]};
+}
+
+// S^T[kb] = K_kb Q^T for one tile (used once, before the pipelined loop).
 template <int D, bool IS_BF16>
-__device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *lk, int l32,
-                                        int g) {
+__device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *kst,
+                                        const LaneAddr<D> &la) {
   using S = Shape16<D>;
 #pragma unroll
   for (int kb = 0; kb < S::NKB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-  for (int kc = 0; kc < S::NKC; ++kc)
-#pragma unroll
-    for (int kb = 0; kb < S::NKB; ++kb) {
-      const u32x4 a =
-          *reinterpret_cast<const u32x4 *>(lk + (kb * 32 + l32) * S::KSTR + kc * 16 + g * 8);
-      s[kb] = mfma_qk<IS_BF16>(a, qf[kc], s[kb]);
-    }
+    for (int kc = 0; kc < S::NKC; ++kc)
+      s[kb] = mfma_qk<IS_BF16>(k_frag<D>(kst, la, kb, kc), qf[kc], kc == 0 ? f32x16{} : s[kb]);
 }
 
 // Per-lane online-softmax state: one query row, half of each tile's keys.
@@ -250,31 +335,24 @@ struct RowState16 {
   float l;             // sum of this lane's rounded weights
 };
 
-// Online-softmax update for one tile of scores, first half: mask (boundary
-// tiles only), row maximum, lazy rescale of the state.
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0, int N, int qrow,
-                                            float qk, int g) {
+// Score register r of block kb belongs to key 32kb + 8(r/4) + 4g + r%4 of the
+// tile (the 32x32 MFMA output layout); masked keys become -inf.
+template <bool CAUSAL>
+__device__ __forceinline__ float mask_score(float x, int key, int N, int qrow) {
+  const bool dead = key >= N || (CAUSAL && key > qrow);
+  return dead ? -INFINITY : x;
+}
+__device__ __forceinline__ int score_key(int n0, int kb, int r, int g) {
+  return n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+// New reference maximum from a tile's row maximum m_tile (base-2 units): the
+// rare rescale of the state, taken by the whole wave when some row's maximum
+// grew by more than kRescaleLog2.
+template <int D>
+__device__ __forceinline__ void rescale(RowState16<D> &st, float m_tile) {
   using S = Shape16<D>;
-  if constexpr (MASK) {  // key tail and/or causal diagonal: hidden keys get -inf
-#pragma unroll
-    for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = n0 + kb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool dead = key >= N || (CAUSAL && key > qrow);
-        s[kb][r] = dead ? -INFINITY : s[kb][r];
-      }
-  }
-  // Row maximum of the scaled scores (qk > 0, so it is max(s) * qk).
-  float mx = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < S::NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-  mx = fmaxf(mx, shfl_xor32(mx));
-  const float m_tile = mx * qk;
-  if (__any(m_tile > st.m + kRescaleLog2)) {  // wave-uniform: some row grew a lot
+  if (__any(m_tile > st.m + kRescaleLog2)) {
     const float m_new = fmaxf(st.m, m_tile);
     const float neg_new = m_new == -INFINITY ? 0.f : -m_new;
     const float alpha = exp2_fast(st.m + neg_new);  // 0 when m was -inf
@@ -288,154 +366,264 @@ __device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0
   }
 }
 
-// One packed P^T dword: weights p = 2^(s*qk - m) of two consecutive score
-// registers rounded to fp16, and their (rounded) sum added to *lsum.
-__device__ __forceinline__ uint32_t exp_pair(float s0, float s1, float qk, float neg_m,
-                                             float *lsum) {
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  const float p0 = exp2_fast(fmaf(s0, qk, neg_m));
-  const float p1 = exp2_fast(fmaf(s1, qk, neg_m));
-  const uint32_t h = pack_f16(p0, p1);
-  *lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, *lsum, false);
-  return h;
+// Mask, row maximum and rescale for a whole tile of scores at once (the
+// first tile; later tiles do this inside phase 2).
+template <int D, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0, int N, int qrow,
+                                            float qk, int g) {
+  using S = Shape16<D>;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < S::NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if constexpr (MASK) s[kb][r] = mask_score<CAUSAL>(s[kb][r], score_key(n0, kb, r, g), N, qrow);
+      mx = fmaxf(mx, s[kb][r]);
+    }
+  rescale<D>(st, max_halves(mx) * qk);  // qk > 0: the max of the scaled scores
 }
 
-// Everything one workgroup iteration touches.
+// Everything the iterations of one wave touch.
 template <int D>
 struct Pipe16 {
-  uint16_t *lds;      // K stage s at lds + s*K_ELEMS, V^T stages after both K stages
+  uint16_t *lds;  // K stages 0..2, then V stages 0..1
   const uint16_t *Kh, *Vh;
-  u32x4 rk[Shape16<D>::K_CHUNKS];  // K tile j+2 in flight
-  u32x4 rv[4];                     // V tile j+1 in flight
-  f32x16 s[Shape16<D>::NKB];       // scores of the tile being normalised
-  int N, n_tiles, qrow, tid, l32, g;
+  LaneAddr<D> la;
+  int N, n_tiles, qrow, g, tid;
+  uint32_t lds_wave;  // LDS byte address of the buffer plus 1024 * wave (uniform)
+  uint32_t k_dma, v_dma;
   float qk;
+
+  __device__ __forceinline__ uint16_t *kstage(int t) const {
+    return lds + (t % kKStages) * Shape16<D>::TILE_ELEMS;
+  }
+  __device__ __forceinline__ uint16_t *vstage(int par) const {
+    return lds + (kKStages + par) * Shape16<D>::TILE_ELEMS;
+  }
+  // Tile copies. Iteration j (reading K_{j+1} and V_j) starts by issuing
+  // V_{j+1}, then K_{j+3}, into the stages V_{j-1} and K_j left (free since
+  // the barrier that ended iteration j-1), and ends by waiting for all but
+  // K_{j+3}: V_{j+1} and K_{j+2} (issued one iteration earlier) have landed.
+  __device__ __forceinline__ void issue_k(int t) const {
+    constexpr int TB = Shape16<D>::TILE_BYTES;
+    dma_tile<D>(tile_rsrc<D>(Kh, t, n_tiles, N), lds_wave + (t % kKStages) * TB, k_dma);
+  }
+  __device__ __forceinline__ void issue_v(int t) const {
+    constexpr int TB = Shape16<D>::TILE_BYTES;
+    dma_tile<D>(tile_rsrc<D>(Vh, t, n_tiles, N), lds_wave + (kKStages + (t & 1)) * TB, v_dma);
+  }
+  // bf16 V_t -> fp16, in place: the 16-byte slots this thread's own copy
+  // wrote (complete once its vmcnt wait has passed).
+  template <bool IS_BF16>
+  __device__ __forceinline__ void convert_v(int t) const {
+    if (!IS_BF16 || t >= n_tiles) return;
+    uint16_t *vs = vstage(t & 1);
+#pragma unroll
+    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) {
+      u32x4 *p = reinterpret_cast<u32x4 *>(vs + c * 2048 + tid * 8);
+      const u32x4 x = *p;
+      u32x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = pack_f16(bf16_lo_to_f32(x[e]), bf16_hi_to_f32(x[e]));
+      *p = y;
+    }
+  }
 };
 
-// LDS reads run this many MFMA steps ahead of their use.
+// LDS operand reads run this many MFMA steps ahead of their use.
 constexpr int kLookahead = 3;
 
-// Iteration j of the software pipeline. On entry: K_{j+1} and V_j are in
-// LDS, S_j is in registers.
-//  phase 0: row maxima of S_j and the (rare) rescale of the state;
-//  phase 1: QK^T of tile j+1 on the matrix cores, one MFMA per step, each
-//           step also computing two weights of tile j on the vector ALUs;
-//  phase 2: P_j V_j, one MFMA per step, the first steps also writing the
-//           prefetched V_{j+1} / K_{j+2} into the LDS stages freed last
-//           iteration.
-// Within a phase the vector work of a step does not depend on the MFMA in
-// flight, so the two units run concurrently; scheduling barriers keep the
-// compiler from regrouping the steps. NEXT = false for the last tile.
-template <int D, bool IS_BF16, bool CAUSAL, bool MASK, bool NEXT>
-__device__ __forceinline__ void pipe_iter(Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf, int j) {
+// Step at which score pair p (P^T dword p % 4 of PV operand p / 4, scores
+// of block p / 8) takes its exponent argument; its exponential follows one
+// step later and its fp16 pack and row sum one more later. The NM1 QK^T steps
+// come first, then the NM2 P.V steps. The first F pairs are spread over the
+// first FS steps, the rest over the steps left before their P.V steps: the
+// QK^T steps finish the blocks of S_{j+1} from the last to the first, and
+// taking S_j's first blocks early lets the later blocks of S_{j+1} reuse
+// their registers (five blocks live at a time for d=128, six for d=64, not
+// eight), while the vector work still spreads over most of the MFMAs.
+template <int D>
+struct PairPlan {
   using S = Shape16<D>;
-  constexpr int BN = S::BN;
+  static constexpr int NM1 = S::NKB * S::NKC;
+  static constexpr int NM2 = S::NT * S::NCB;
+  static constexpr int NP = S::NT * 4;
+  static constexpr int F = D == 128 ? 8 : 16;
+  static constexpr int FS = D == 128 ? 8 : 12;
+  static constexpr int deadline(int p) { return NM1 + (p >> 2) * S::NCB - 1; }
+  static constexpr int LAST = deadline(NP - 1) - 2;
+  static constexpr int start(int p) {
+    return p < F ? p * FS / F : FS + (p - F) * (LAST - FS) / (NP - 1 - F);
+  }
+  static constexpr bool valid() {
+    for (int p = 0; p < NP; ++p)
+      if (start(p) + 2 > deadline(p) || (p > 0 && start(p) < start(p - 1))) return false;
+    return start(NP - 1) == LAST;
+  }
+  static_assert(valid(), "every pair is packed before its P.V step");
+  // First pair starting at step i or later, and the most pairs one step starts.
+  static constexpr int first_at(int i) {
+    int p = 0;
+    while (p < NP && start(p) < i) ++p;
+    return p;
+  }
+  static constexpr int max_per_step() {
+    int m = 0;
+    for (int i = 0; i <= LAST; ++i) m = first_at(i + 1) - first_at(i) > m ? first_at(i + 1) - first_at(i) : m;
+    return m;
+  }
+  static constexpr int MAXP = max_per_step();
+};
+
+// Iteration j of one wave: on entry K_{j+1} and V_j are in LDS and S_j (s)
+// is in registers, masked, its maximum folded into the reference. Steps
+// 0..NM1-1: s_next[kb] += K_kb,kc Q_kc^T (NEXT; kb = NKB-1 - i / NKC,
+// kc = i % NKC). Steps NM1..NM1+NM2-1: acc[cb] += V^T_cb,t P^T_t
+// (t = i' / NCB, cb = i' % NCB). Alongside, on the vector ALUs: the
+// weights of S_j (three stages per score pair, in successive steps, so no
+// instruction waits on the one before) and, in the P.V steps, the mask
+// (MASK_NEXT) and row maximum of S_{j+1}, blocks in the order they were
+// finished. Then the (rare) rescale for S_{j+1}. Scheduling barriers keep
+// the compiler from regrouping the steps. VPAR is j's parity when known at
+// compile time (-1 otherwise), which makes the V stage addresses constants.
+template <int D, bool IS_BF16, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
+__device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
+                                          int j, f32x16 (&s)[Shape16<D>::NKB],
+                                          f32x16 (&s_next)[Shape16<D>::NKB]) {
+  using S = Shape16<D>;
+  using PP = PairPlan<D>;
   constexpr int LA = kLookahead;
-  const bool k_next2 = NEXT && j + 2 < pp.n_tiles;
-  const int l32 = pp.l32, g = pp.g;
-  // Stage offsets are selected as integers so the pointers stay in LDS.
-  uint16_t *const k_this = pp.lds + (j & 1) * S::K_ELEMS;
-  uint16_t *const k_next = pp.lds + ((j + 1) & 1) * S::K_ELEMS;
-  uint16_t *const v_this = pp.lds + 2 * S::K_ELEMS + (j & 1) * S::V_ELEMS;
-  uint16_t *const v_next = pp.lds + 2 * S::K_ELEMS + ((j + 1) & 1) * S::V_ELEMS;
-  if (NEXT) {
-    if (k_next2) load_k16<D>(pp.rk, pp.Kh, (j + 2) * BN, pp.N, pp.tid);
-    load_v16<D>(pp.rv, pp.Vh, (j + 1) * BN, pp.N, pp.tid);
-  }
-
-  // ---- phase 0
-  softmax_max<D, CAUSAL, MASK>(st, pp.s, j * BN, pp.N, pp.qrow, pp.qk, g);
-
-  // ---- phase 1: MFMA step i accumulates s_next[kb] += K_kb,kc Q_kc^T with
-  // kc = i / NKB, kb = i % NKB (alternating accumulators), and packs the
-  // next PPS P^T dwords of tile j.
-  constexpr int NM1 = S::NKB * S::NKC;
-  constexpr int PPS = S::NT * 4 / NM1;  // P^T dwords per step (1 for d=128, 2 for d=64)
-  static_assert(PPS * NM1 == S::NT * 4, "P^T dwords split evenly over the QK^T MFMAs");
-  f32x16 s_next[S::NKB];
+  constexpr int NM1 = PP::NM1, NM2 = PP::NM2, NP = PP::NP;
+  constexpr int NS = NM1 + NM2;
+  constexpr int NE = S::NKB * 16;  // scores of S_{j+1} per lane
+  static_assert(NE % NM2 == 0, "scores split evenly over the P.V steps");
+  constexpr int EPS = NE / NM2;
+  const uint16_t *k_next = pp.kstage(j + 1);
+  const uint16_t *v_this = pp.vstage(VPAR >= 0 ? VPAR : (j & 1));
+  const int n1 = (j + 1) * S::BN;
   u32x4 pf[S::NT];
-  float lsum = 0.f;
+  float xa[NP][2], ea[NP][2];  // exponent arguments, exponentials
+  float lsum = 0.f, mx = -INFINITY;
   const float qk = pp.qk, neg_m = st.neg_m;
-  u32x4 kf[LA + 1];
-  const uint16_t *kbase = k_next + l32 * S::KSTR + g * 8;
-  if (NEXT) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  // LDS operands run LA steps ahead; fr[i % (LA + 1)] holds step i's.
+  u32x4 fr[LA + 1];
+  auto operand = [&](int i) -> u32x4 {
+    if (i < NM1) return k_frag<D>(k_next, pp.la, S::NKB - 1 - i / S::NKC, i % S::NKC);
+    const int i2 = i - NM1;
+    return v_frag<D>(v_this, pp.la, i2 / S::NCB, i2 % S::NCB);
+  };
+  const int first = NEXT ? 0 : NM1;  // the last tile has no QK^T steps
 #pragma unroll
-    for (int kb = 0; kb < S::NKB; ++kb)
+  for (int i = 0; i < LA; ++i)
+    if (first + i < NS) fr[(first + i) % (LA + 1)] = operand(first + i);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s_next[kb][r] = 0.f;
-#pragma unroll
-    for (int i = 0; i < LA; ++i)
-      kf[i] = *reinterpret_cast<const u32x4 *>(kbase + (i % S::NKB) * 32 * S::KSTR +
-                                               (i / S::NKB) * 16);
-  }
-#pragma unroll
-  for (int i = 0; i < NM1; ++i) {
-    if (NEXT) {
+  for (int i = 0; i < NS; ++i) {
+    if (i >= first) {
       const int ia = i + LA;
-      if (ia < NM1)
-        kf[ia % (LA + 1)] = *reinterpret_cast<const u32x4 *>(
-            kbase + (ia % S::NKB) * 32 * S::KSTR + (ia / S::NKB) * 16);
-      const int kb = i % S::NKB, kc = i / S::NKB;
-      s_next[kb] = mfma_qk<IS_BF16>(kf[i % (LA + 1)], qf[kc], s_next[kb]);
+      if (ia < NS) fr[ia % (LA + 1)] = operand(ia);
+      if (i < NM1) {
+        const int kb = S::NKB - 1 - i / S::NKC, kc = i % S::NKC;
+        s_next[kb] = mfma_qk<IS_BF16>(fr[i % (LA + 1)], qf[kc], kc == 0 ? f32x16{} : s_next[kb]);
+      } else {
+        const int i2 = i - NM1, cb = i2 % S::NCB, t = i2 / S::NCB;
+        st.acc[cb] = mfma_pv(fr[i % (LA + 1)], pf[t], st.acc[cb]);
+      }
     }
 #pragma unroll
-    for (int q = 0; q < PPS; ++q) {
-      const int dw = i * PPS + q, t = dw >> 2, w = dw & 3;
-      const int kb = t >> 1, r = 8 * (t & 1) + 2 * w;
-      pf[t][w] = exp_pair(pp.s[kb][r], pp.s[kb][r + 1], qk, neg_m, &lsum);
-      asm volatile("" ::"v"(pf[t][w]));  // keep this step's weights in this step
+    for (int q = 0; q < PP::MAXP; ++q) {
+      const int pa = PP::first_at(i) + q;  // exponent arguments
+      if (pa < NP && PP::start(pa) == i) {
+        const int t = pa >> 2, kb = t >> 1, r = 8 * (t & 1) + 2 * (pa & 3);
+        xa[pa][0] = fmaf(s[kb][r], qk, neg_m);
+        xa[pa][1] = fmaf(s[kb][r + 1], qk, neg_m);
+      }
+      const int pb = PP::first_at(i - 1) + q;  // exponentials
+      if (i >= 1 && pb < NP && PP::start(pb) == i - 1) {
+        ea[pb][0] = exp2_fast(xa[pb][0]);
+        ea[pb][1] = exp2_fast(xa[pb][1]);
+      }
+      const int pc = PP::first_at(i - 2) + q;  // fp16 pack and row sum
+      if (i >= 2 && pc < NP && PP::start(pc) == i - 2) {
+        const uint32_t h = pack_f16(ea[pc][0], ea[pc][1]);
+        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, lsum, false);
+        pf[pc >> 2][pc & 3] = h;
+        asm volatile("" ::"v"(h));  // keep this pair's weights in this step
+      }
+    }
+    if (NEXT && i >= NM1) {
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        // blocks in the order the QK^T steps finished them (kb descending)
+        const int el = (i - NM1) * EPS + e, kb = S::NKB - 1 - (el >> 4), r = el & 15;
+        if (MASK_NEXT)
+          s_next[kb][r] = mask_score<CAUSAL>(s_next[kb][r], score_key(n1, kb, r, pp.g), pp.N, pp.qrow);
+        mx = fmaxf(mx, s_next[kb][r]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
   st.l += lsum;
+  if (NEXT) rescale<D>(st, max_halves(mx) * qk);  // after P_j V_j: acc and l hold tile j
+}
 
-  // ---- phase 2: MFMA step i accumulates acc[cb] += V^T_cb,t P^T_t with
-  // t = i / NCB, cb = i % NCB.
-  constexpr int NM2 = S::NT * S::NCB;
-  u32x4 vf[LA + 1];
-  const uint16_t *vbase = v_this + l32 * S::VSTR + 8 * g;
-#pragma unroll
-  for (int i = 0; i < LA; ++i)
-    vf[i] = *reinterpret_cast<const u32x4 *>(vbase + (i % S::NCB) * 32 * S::VSTR +
-                                             16 * (i / S::NCB));
-#pragma unroll
-  for (int i = 0; i < NM2; ++i) {
-    const int ia = i + LA;
-    if (ia < NM2)
-      vf[ia % (LA + 1)] = *reinterpret_cast<const u32x4 *>(
-          vbase + (ia % S::NCB) * 32 * S::VSTR + 16 * (ia / S::NCB));
-    const int cb = i % S::NCB, t = i / S::NCB;
-    st.acc[cb] = mfma_pv(vf[i % (LA + 1)], pf[t], st.acc[cb]);
-    if (NEXT) {
-      if (i < 4) store_v16_part<D, IS_BF16>(pp.rv, v_next, pp.tid, i);
-      if (i >= 4 && i < 4 + S::K_CHUNKS && k_next2)
-        store_k16_chunk<D>(pp.rk, k_this, pp.tid, i - 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+// All iterations of one wave. nw: key tiles this wave visits, nfw: leading
+// tiles it needs no mask for; the workgroup runs pp.n_tiles iterations, each
+// ending with the copies' wait, the bf16 conversion and a barrier.
+template <int D, bool IS_BF16, bool CAUSAL>
+__device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
+                                         f32x16 (&sa)[Shape16<D>::NKB],
+                                         f32x16 (&sb)[Shape16<D>::NKB], int nw, int nfw) {
+  using S = Shape16<D>;
+  const int n = pp.n_tiles;
+#define ITER(jj, work)                                                  \
+  do {                                                                  \
+    pp.issue_v((jj) + 1);                                               \
+    pp.issue_k((jj) + 3);                                               \
+    work;                                                               \
+    wait_vmcnt<S::DMA_INS>(); /* all but K_{j+3} have landed */        \
+    pp.template convert_v<IS_BF16>((jj) + 1);                           \
+    lds_barrier();                                                      \
+  } while (0)
+  int j = 0;
+  const int n_a = max(min(nfw, nw) - 1, 0);  // tiles j < n_a have an unmasked successor
+  for (; j + 2 <= n_a; j += 2) {
+    ITER(j, (iteration<D, IS_BF16, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
+    ITER(j + 1, (iteration<D, IS_BF16, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
   }
-  if (NEXT) {
+  if (j < n_a) {  // odd count of unmasked successors
+    ITER(j, (iteration<D, IS_BF16, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
-    for (int kb = 0; kb < S::NKB; ++kb) pp.s[kb] = s_next[kb];
-    __syncthreads();
+    for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
+    ++j;
   }
+  for (; j < nw - 1; ++j) {
+    ITER(j, (iteration<D, IS_BF16, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
+#pragma unroll
+    for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
+  }
+  ITER(j, (iteration<D, IS_BF16, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
+  for (++j; j < n; ++j) ITER(j, (void)0);  // tiles past this wave's rows
+#undef ITER
 }
 
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
+__global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
   constexpr int NCB = S::NCB;
   constexpr int NKC = S::NKC;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * S::K_ELEMS + 2 * S::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[(kKStages + kVStages) * S::TILE_ELEMS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   int bh, qt;
   work_item<CAUSAL>(p, bh, qt);
   const int N = p.N;
-  const int m0 = qt * kBlockM;
+  const int m0 = qt * kBlockM16;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + head;
 
@@ -443,27 +631,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
   pp.lds = lds;
   pp.Kh = static_cast<const uint16_t *>(p.k) + head;
   pp.Vh = static_cast<const uint16_t *>(p.v) + head;
+  pp.la = lane_addr<D>(lane);
   pp.N = N;
-  pp.tid = tid;
-  pp.l32 = l32;
   pp.g = g;
+  pp.tid = tid;
   pp.qk = p.qk;
-  // This lane's query row; rows past N read as zero and are never stored.
-  pp.qrow = m0 + wave * 32 + l32;
+  pp.lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 1024);
+  pp.k_dma = dma_offset<D, false>(tid);
+  pp.v_dma = dma_offset<D, true>(tid);
+  // This lane's query row; rows past N use row N-1's data and are never stored.
+  const int r0 = m0 + wave * 32;  // first row of this wave
+  pp.qrow = r0 + l32;
+  const int qsrc = min(pp.qrow, N - 1);
 
   u32x4 qf[NKC];
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc)
-    qf[kc] = pp.qrow < N
-                 ? *reinterpret_cast<const u32x4 *>(Qh + (size_t)pp.qrow * D + kc * 16 + g * 8)
-                 : u32x4{0u, 0u, 0u, 0u};
+    qf[kc] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)qsrc * D + kc * 16 + g * 8);
 
-  // KV tiles to visit. Causal: only tiles holding some key <= the block's
-  // last row. Tiles [0, n_full) need no mask at all.
+  // Key tiles to visit: for the workgroup (copies, barriers) and for this
+  // wave (compute). Causal: only tiles holding some key <= the last row.
+  // Tiles [0, nfw) need no mask for this wave.
   const int n_all = (N + BN - 1) / BN;
-  const int n_tiles = CAUSAL ? min(n_all, (m0 + kBlockM + BN - 1) / BN) : n_all;
-  int n_full = N / BN;
-  if (CAUSAL) n_full = min(n_full, (m0 + 1) / BN);
+  const int n_tiles = CAUSAL ? min(n_all, (m0 + kBlockM16 + BN - 1) / BN) : n_all;
+  const int nw = CAUSAL ? min(n_all, (r0 + 32 + BN - 1) / BN) : n_all;
+  int nfw = N / BN;
+  if (CAUSAL) nfw = min(nfw, (r0 + 1) / BN);
   pp.n_tiles = n_tiles;
 
   RowState16<D> st;
@@ -475,29 +668,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_16(FwdParams p) {
   st.neg_m = 0.f;
   st.l = 0.f;
 
-  // Prologue: K_0, V_0 and K_1 into LDS, then S_0.
-  load_k16<D>(pp.rk, pp.Kh, 0, N, tid);
-  load_v16<D>(pp.rv, pp.Vh, 0, N, tid);
-  store_k16<D>(pp.rk, lds, tid);
-  store_v16<D, IS_BF16>(pp.rv, lds + 2 * S::K_ELEMS, tid);
-  if (n_tiles > 1) {
-    load_k16<D>(pp.rk, pp.Kh, BN, N, tid);
-    store_k16<D>(pp.rk, lds + S::K_ELEMS, tid);
-  }
-  __syncthreads();
-  qk_tile<D, IS_BF16>(pp.s, qf, lds, l32, g);
-
-  int j = 0;
-  const int n_pipe = min(n_full, n_tiles - 1);  // unmasked tiles with a successor
-  for (; j < n_pipe; ++j) pipe_iter<D, IS_BF16, CAUSAL, false, true>(pp, st, qf, j);
-  for (; j < n_tiles - 1; ++j) pipe_iter<D, IS_BF16, CAUSAL, true, true>(pp, st, qf, j);
-  if (j < n_full)
-    pipe_iter<D, IS_BF16, CAUSAL, false, false>(pp, st, qf, j);
+  // Prologue: V_0 and K_0..K_2 on their way; V_0 (converted) and S_0 once
+  // V_0 and K_0 are in; K_1 in before iteration 0.
+  pp.issue_v(0);
+  pp.issue_k(0);
+  pp.issue_k(1);
+  pp.issue_k(2);
+  wait_vmcnt<2 * S::DMA_INS>();  // V_0, K_0
+  pp.template convert_v<IS_BF16>(0);
+  lds_barrier();
+  f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
+  qk_tile<D, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
+  if (nfw == 0)
+    softmax_max<D, CAUSAL, true>(st, sa, 0, N, pp.qrow, pp.qk, g);
   else
-    pipe_iter<D, IS_BF16, CAUSAL, true, false>(pp, st, qf, j);
+    softmax_max<D, CAUSAL, false>(st, sa, 0, N, pp.qrow, pp.qk, g);
+  wait_vmcnt<S::DMA_INS>();  // K_1
+  lds_barrier();
+
+  run_wave<D, IS_BF16, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
+
+  // Copies issued for tiles past the end (empty byte ranges) retire before
+  // the workgroup's LDS can be handed to another one.
+  wait_vmcnt<0>();
 
   // Epilogue: combine the two key halves of the row sum, divide once, LSE.
-  const float l_tot = st.l + shfl_xor32(st.l);
+  const float l_tot = sum_halves(st.l);
   const float l_safe = l_tot > 0.f ? l_tot : 1.f;
   const float inv = 1.0f / l_safe;
   const int qrow = pp.qrow;
