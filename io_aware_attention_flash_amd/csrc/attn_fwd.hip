@@ -226,14 +226,6 @@ __device__ __forceinline__ uint32_t dma_offset(int tid) {
   const int swz = IS_V ? swz_v<D>(row0) : swz_k<D>(row0);
   return row0 * D * 2 + (((tid % CPR) ^ swz) << 4);
 }
-// stage_byte: LDS byte address of the stage plus 1024 * wave (wave-uniform).
-template <int D>
-__device__ __forceinline__ void dma_tile(u32x4 rsrc, uint32_t stage_byte, uint32_t voff) {
-#pragma unroll
-  for (int c = 0; c < Shape16<D>::DMA_INS; ++c)
-    dma16_to_lds(rsrc, stage_byte + c * 4096, voff + c * 4096);
-}
-
 // Wait until at most N vector-memory instructions of this wave are
 // outstanding (they retire in order).
 template <int N>
@@ -383,6 +375,15 @@ __device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0
   rescale<D>(st, max_halves(mx) * qk);  // qk > 0: the max of the scaled scores
 }
 
+// Eight bf16 values -> eight fp16 values (round to nearest even; exact for
+// |v| in [2^-14, 65504]).
+__device__ __forceinline__ u32x4 to_f16(u32x4 x) {
+  u32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = pack_f16(bf16_lo_to_f32(x[e]), bf16_hi_to_f32(x[e]));
+  return y;
+}
+
 // Everything the iterations of one wave touch.
 template <int D>
 struct Pipe16 {
@@ -400,33 +401,43 @@ struct Pipe16 {
   __device__ __forceinline__ uint16_t *vstage(int par) const {
     return lds + (kKStages + par) * Shape16<D>::TILE_ELEMS;
   }
-  // Tile copies. Iteration j (reading K_{j+1} and V_j) starts by issuing
+  // Tile copies. Iteration j reads K_{j+1} and V_j. Its first steps issue
   // V_{j+1}, then K_{j+3}, into the stages V_{j-1} and K_j left (free since
-  // the barrier that ended iteration j-1), and ends by waiting for all but
-  // K_{j+3}: V_{j+1} and K_{j+2} (issued one iteration earlier) have landed.
-  __device__ __forceinline__ void issue_k(int t) const {
+  // the barrier that ended iteration j-1); a late step waits for V_{j+1}
+  // and converts it (bf16); the iteration ends by waiting for all but
+  // K_{j+3}, so K_{j+2} (issued one iteration earlier) has landed too.
+  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<D>(Kh, t, n_tiles, N); }
+  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<D>(Vh, t, n_tiles, N); }
+  // Instruction c of the copy of K_t / V_t (descriptor r).
+  __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma_tile<D>(tile_rsrc<D>(Kh, t, n_tiles, N), lds_wave + (t % kKStages) * TB, k_dma);
+    dma16_to_lds(r, lds_wave + (t % kKStages) * TB + c * 4096, k_dma + c * 4096);
+  }
+  __device__ __forceinline__ void copy_v(u32x4 r, int t, int c) const {
+    constexpr int TB = Shape16<D>::TILE_BYTES;
+    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * 4096, v_dma + c * 4096);
+  }
+  __device__ __forceinline__ void issue_k(int t) const {
+    const u32x4 r = k_rsrc(t);
+#pragma unroll
+    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) copy_k(r, t, c);
   }
   __device__ __forceinline__ void issue_v(int t) const {
-    constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma_tile<D>(tile_rsrc<D>(Vh, t, n_tiles, N), lds_wave + (kKStages + (t & 1)) * TB, v_dma);
+    const u32x4 r = v_rsrc(t);
+#pragma unroll
+    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) copy_v(r, t, c);
   }
-  // bf16 V_t -> fp16, in place: the 16-byte slots this thread's own copy
-  // wrote (complete once its vmcnt wait has passed).
+  // 16-byte slot c of the ones this thread's own copy of V_t wrote: after
+  // the copy has landed (this wave's vmcnt wait), the thread converts them
+  // from bf16 to fp16 in place.
+  __device__ __forceinline__ u32x4 *v_slot(int t, int c) const {
+    return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * 2048 + tid * 8);
+  }
   template <bool IS_BF16>
   __device__ __forceinline__ void convert_v(int t) const {
     if (!IS_BF16 || t >= n_tiles) return;
-    uint16_t *vs = vstage(t & 1);
 #pragma unroll
-    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) {
-      u32x4 *p = reinterpret_cast<u32x4 *>(vs + c * 2048 + tid * 8);
-      const u32x4 x = *p;
-      u32x4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = pack_f16(bf16_lo_to_f32(x[e]), bf16_hi_to_f32(x[e]));
-      *p = y;
-    }
+    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) *v_slot(t, c) = to_f16(*v_slot(t, c));
   }
 };
 
@@ -484,8 +495,12 @@ struct PairPlan {
 // instruction waits on the one before) and, in the P.V steps, the mask
 // (MASK_NEXT) and row maximum of S_{j+1}, blocks in the order they were
 // finished. Then the (rare) rescale for S_{j+1}. Scheduling barriers keep
-// the compiler from regrouping the steps. VPAR is j's parity when known at
-// compile time (-1 otherwise), which makes the V stage addresses constants.
+// the compiler from regrouping the steps. The first 2 DMA_INS steps also
+// issue the copies of V_{j+1} and K_{j+3}, one instruction each; step CW
+// waits for V_{j+1} and the steps after it convert it (bf16), one 16-byte
+// slot per two steps (load, then convert and store). VPAR is j's parity
+// when known at compile time (-1 otherwise), which makes the V stage
+// addresses constants.
 template <int D, bool IS_BF16, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
 __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
                                           int j, f32x16 (&s)[Shape16<D>::NKB],
@@ -508,12 +523,17 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   // LDS operands run LA steps ahead; fr[i % (LA + 1)] holds step i's.
   u32x4 fr[LA + 1];
+  constexpr int NI = S::DMA_INS;
+  constexpr int CW = NS - 2 * NI - 2;  // conversion steps CW .. CW + 2 NI - 1
+  static_assert(CW >= 2 * NI, "V_{j+1} is converted after its copy was issued");
+  u32x4 cv[NI];
   auto operand = [&](int i) -> u32x4 {
     if (i < NM1) return k_frag<D>(k_next, pp.la, S::NKB - 1 - i / S::NKC, i % S::NKC);
     const int i2 = i - NM1;
     return v_frag<D>(v_this, pp.la, i2 / S::NCB, i2 % S::NCB);
   };
   const int first = NEXT ? 0 : NM1;  // the last tile has no QK^T steps
+  const u32x4 dv_r = pp.v_rsrc(j + 1), dk_r = pp.k_rsrc(j + 3);
 #pragma unroll
   for (int i = 0; i < LA; ++i)
     if (first + i < NS) fr[(first + i) % (LA + 1)] = operand(first + i);
@@ -551,6 +571,18 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
         asm volatile("" ::"v"(h));  // keep this pair's weights in this step
       }
     }
+    if (IS_BF16 && i >= CW && i < CW + 2 * NI) {
+      const int c = (i - CW) >> 1;
+      if (i == CW) wait_vmcnt<NI>();  // V_{j+1} (issued before K_{j+3}) is in
+      if (j + 1 < pp.n_tiles) {
+        if (((i - CW) & 1) == 0)
+          cv[c] = *pp.v_slot(j + 1, c);
+        else
+          *pp.v_slot(j + 1, c) = to_f16(cv[c]);
+      }
+    }
+    if (i < S::DMA_INS) pp.copy_v(dv_r, j + 1, i);
+    if (i >= S::DMA_INS && i < 2 * S::DMA_INS) pp.copy_k(dk_r, j + 3, i - S::DMA_INS);
     if (NEXT && i >= NM1) {
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
@@ -576,34 +608,38 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
                                          f32x16 (&sb)[Shape16<D>::NKB], int nw, int nfw) {
   using S = Shape16<D>;
   const int n = pp.n_tiles;
-#define ITER(jj, work)                                                  \
-  do {                                                                  \
-    pp.issue_v((jj) + 1);                                               \
-    pp.issue_k((jj) + 3);                                               \
-    work;                                                               \
-    wait_vmcnt<S::DMA_INS>(); /* all but K_{j+3} have landed */        \
-    pp.template convert_v<IS_BF16>((jj) + 1);                           \
-    lds_barrier();                                                      \
+#define ITER(work)                                               \
+  do {                                                           \
+    work;                                                        \
+    wait_vmcnt<S::DMA_INS>(); /* all but K_{j+3} have landed */ \
+    lds_barrier();                                               \
   } while (0)
   int j = 0;
   const int n_a = max(min(nfw, nw) - 1, 0);  // tiles j < n_a have an unmasked successor
   for (; j + 2 <= n_a; j += 2) {
-    ITER(j, (iteration<D, IS_BF16, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
-    ITER(j + 1, (iteration<D, IS_BF16, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
+    ITER((iteration<D, IS_BF16, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
   }
   if (j < n_a) {  // odd count of unmasked successors
-    ITER(j, (iteration<D, IS_BF16, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
     ++j;
   }
   for (; j < nw - 1; ++j) {
-    ITER(j, (iteration<D, IS_BF16, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
   }
-  ITER(j, (iteration<D, IS_BF16, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
-  for (++j; j < n; ++j) ITER(j, (void)0);  // tiles past this wave's rows
+  ITER((iteration<D, IS_BF16, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
+  // Tiles past this wave's rows: the same copies, conversion and waits.
+  for (++j; j < n; ++j) {
+    pp.issue_v(j + 1);
+    pp.issue_k(j + 3);
+    wait_vmcnt<S::DMA_INS>();
+    pp.template convert_v<IS_BF16>(j + 1);
+    lds_barrier();
+  }
 #undef ITER
 }
 
