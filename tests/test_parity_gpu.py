@@ -75,6 +75,14 @@ SMALL_CASES = [
     (1, 2, 517, 128, "bf16", True, 3.0),
     (1, 2, 640, 64, "f16", True, 1.0),
     (1, 1, 1000, 128, "bf16", False, 3.0),
+    # tile edges: d=128 uses 64-key tiles, d=64 128-key tiles; 128 query rows per workgroup
+    (1, 2, 64, 128, "f16", False, 1.0),
+    (1, 2, 128, 64, "bf16", True, 1.0),
+    (1, 2, 129, 64, "bf16", False, 1.0),
+    (1, 1, 191, 128, "bf16", True, 1.0),
+    (1, 1, 192, 128, "f16", True, 1.0),
+    (1, 1, 385, 64, "f16", True, 2.0),
+    (3, 5, 97, 128, "bf16", True, 1.0),
 ]
 
 
