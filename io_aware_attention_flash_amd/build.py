@@ -3,9 +3,13 @@
     python -m io_aware_attention_flash_amd.build
 
 hipcc cross-compiles for gfx950 on a machine without a GPU. Packed-fp32
-instructions are disabled for all device code.
+instructions are disabled for all device code. The kernels' per-step loops
+are fully unrolled (their register arrays are indexed by compile-time step
+numbers); the unroll budget is raised so they stay so, and the build fails
+if any kernel ends up using scratch memory.
 """
 import os
+import re
 import subprocess
 import sys
 
@@ -19,8 +23,24 @@ ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
 HIPCC_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-shared", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=65536",
+    "-Rpass-analysis=kernel-resource-usage",
     "-Wall", "-Wno-unused-function",
 ]
+
+
+def scratch_users(remarks):
+    """Kernels whose resource-usage remarks report scratch (private) memory."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            bad.append((name, int(m.group(1))))
+    return bad
 
 
 def build(verbose=False, extra=()):
@@ -33,6 +53,11 @@ def build(verbose=False, extra=()):
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building %s" % LIB)
+    bad = scratch_users(res.stderr)
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError("kernels use scratch memory (a step loop was not unrolled or "
+                           "registers spilled): %s" % ", ".join("%s (%d B/lane)" % b for b in bad))
     os.replace(tmp, LIB)
     return LIB
 

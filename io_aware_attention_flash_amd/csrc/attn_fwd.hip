@@ -132,7 +132,7 @@ __device__ __forceinline__ float sum_halves(float x) {
 constexpr int kWaves16 = 4;
 constexpr int kThreads16 = kWaves16 * 64;
 constexpr int kBlockM16 = kWaves16 * 32;
-constexpr int kKStages = 3;
+constexpr int kKStages = 2;
 constexpr int kVStages = 2;
 
 template <int D>
@@ -387,35 +387,36 @@ __device__ __forceinline__ u32x4 to_f16(u32x4 x) {
 // Everything the iterations of one wave touch.
 template <int D>
 struct Pipe16 {
-  uint16_t *lds;  // K stages 0..2, then V stages 0..1
+  uint16_t *lds;  // K stages 0..1, then V stages 0..1 (tile t in stage t % 2)
   const uint16_t *Kh, *Vh;
   LaneAddr<D> la;
   int N, n_tiles, qrow, g, tid;
   uint32_t lds_wave;  // LDS byte address of the buffer plus 1024 * wave (uniform)
-  uint32_t k_dma, v_dma;
+  // Source offsets of this thread's 16 bytes in copy instruction c (kept in
+  // registers: the descriptor's range check applies to them).
+  uint32_t k_dma[Shape16<D>::DMA_INS], v_dma[Shape16<D>::DMA_INS];
   float qk;
 
-  __device__ __forceinline__ uint16_t *kstage(int t) const {
-    return lds + (t % kKStages) * Shape16<D>::TILE_ELEMS;
+  __device__ __forceinline__ uint16_t *kstage(int par) const {
+    return lds + par * Shape16<D>::TILE_ELEMS;
   }
   __device__ __forceinline__ uint16_t *vstage(int par) const {
     return lds + (kKStages + par) * Shape16<D>::TILE_ELEMS;
   }
   // Tile copies. Iteration j reads K_{j+1} and V_j. Its first steps issue
-  // V_{j+1}, then K_{j+3}, into the stages V_{j-1} and K_j left (free since
+  // V_{j+1}, then K_{j+2}, into the stages V_{j-1} and K_j left (free since
   // the barrier that ended iteration j-1); a late step waits for V_{j+1}
-  // and converts it (bf16); the iteration ends by waiting for all but
-  // K_{j+3}, so K_{j+2} (issued one iteration earlier) has landed too.
+  // and converts it (bf16); the iteration ends by waiting for K_{j+2}.
   __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<D>(Kh, t, n_tiles, N); }
   __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<D>(Vh, t, n_tiles, N); }
   // Instruction c of the copy of K_t / V_t (descriptor r).
   __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (t % kKStages) * TB + c * 4096, k_dma + c * 4096);
+    dma16_to_lds(r, lds_wave + (t & 1) * TB + c * 4096, k_dma[c]);
   }
   __device__ __forceinline__ void copy_v(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * 4096, v_dma + c * 4096);
+    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * 4096, v_dma[c]);
   }
   __device__ __forceinline__ void issue_k(int t) const {
     const u32x4 r = k_rsrc(t);
@@ -496,7 +497,7 @@ struct PairPlan {
 // (MASK_NEXT) and row maximum of S_{j+1}, blocks in the order they were
 // finished. Then the (rare) rescale for S_{j+1}. Scheduling barriers keep
 // the compiler from regrouping the steps. The first 2 DMA_INS steps also
-// issue the copies of V_{j+1} and K_{j+3}, one instruction each; step CW
+// issue the copies of V_{j+1} and K_{j+2}, one instruction each; step CW
 // waits for V_{j+1} and the steps after it convert it (bf16), one 16-byte
 // slot per two steps (load, then convert and store). VPAR is j's parity
 // when known at compile time (-1 otherwise), which makes the V stage
@@ -513,7 +514,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
   constexpr int NE = S::NKB * 16;  // scores of S_{j+1} per lane
   static_assert(NE % NM2 == 0, "scores split evenly over the P.V steps");
   constexpr int EPS = NE / NM2;
-  const uint16_t *k_next = pp.kstage(j + 1);
+  const uint16_t *k_next = pp.kstage(VPAR >= 0 ? 1 - VPAR : ((j + 1) & 1));
   const uint16_t *v_this = pp.vstage(VPAR >= 0 ? VPAR : (j & 1));
   const int n1 = (j + 1) * S::BN;
   u32x4 pf[S::NT];
@@ -524,7 +525,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
   // LDS operands run LA steps ahead; fr[i % (LA + 1)] holds step i's.
   u32x4 fr[LA + 1];
   constexpr int NI = S::DMA_INS;
-  constexpr int CW = NS - 2 * NI - 2;  // conversion steps CW .. CW + 2 NI - 1
+  constexpr int CW = NS - 2 * NI - 2;  // conversion steps CW .. CW + 2 NI
   static_assert(CW >= 2 * NI, "V_{j+1} is converted after its copy was issued");
   u32x4 cv[NI];
   auto operand = [&](int i) -> u32x4 {
@@ -533,7 +534,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
     return v_frag<D>(v_this, pp.la, i2 / S::NCB, i2 % S::NCB);
   };
   const int first = NEXT ? 0 : NM1;  // the last tile has no QK^T steps
-  const u32x4 dv_r = pp.v_rsrc(j + 1), dk_r = pp.k_rsrc(j + 3);
+  const u32x4 dv_r = pp.v_rsrc(j + 1), dk_r = pp.k_rsrc(j + 2);
 #pragma unroll
   for (int i = 0; i < LA; ++i)
     if (first + i < NS) fr[(first + i) % (LA + 1)] = operand(first + i);
@@ -568,21 +569,29 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
         const uint32_t h = pack_f16(ea[pc][0], ea[pc][1]);
         lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, h), ones, lsum, false);
         pf[pc >> 2][pc & 3] = h;
-        asm volatile("" ::"v"(h));  // keep this pair's weights in this step
+        // keep this pair's weights and its share of the row sum in this step
+        asm volatile("" : "+v"(lsum) : "v"(h));
       }
     }
-    if (IS_BF16 && i >= CW && i < CW + 2 * NI) {
-      const int c = (i - CW) >> 1;
-      if (i == CW) wait_vmcnt<NI>();  // V_{j+1} (issued before K_{j+3}) is in
-      if (j + 1 < pp.n_tiles) {
-        if (((i - CW) & 1) == 0)
-          cv[c] = *pp.v_slot(j + 1, c);
-        else
-          *pp.v_slot(j + 1, c) = to_f16(cv[c]);
+    if (IS_BF16 && i >= CW && i <= CW + 2 * NI) {
+      // Slot c is read at step CW + 2c; its first two dwords are converted
+      // one step later, the other two and the store one more later. Past
+      // the last tile the copy brought zeros, which convert harmlessly.
+      const int k = i - CW;
+      if (k == 0) wait_vmcnt<NI>();  // V_{j+1} (issued before K_{j+2}) is in
+      if ((k & 1) == 0 && k / 2 < NI) cv[k / 2] = *pp.v_slot(j + 1, k / 2);
+      if (k >= 1) {
+        const int c = (k - 1) >> 1, e0 = 2 * ((k - 1) & 1);
+#pragma unroll
+        for (int e = e0; e < e0 + 2; ++e) {
+          cv[c][e] = pack_f16(bf16_lo_to_f32(cv[c][e]), bf16_hi_to_f32(cv[c][e]));
+          asm volatile("" : "+v"(cv[c][e]));
+        }
+        if (e0 == 2) *pp.v_slot(j + 1, c) = cv[c];
       }
     }
     if (i < S::DMA_INS) pp.copy_v(dv_r, j + 1, i);
-    if (i >= S::DMA_INS && i < 2 * S::DMA_INS) pp.copy_k(dk_r, j + 3, i - S::DMA_INS);
+    if (i >= S::DMA_INS && i < 2 * S::DMA_INS) pp.copy_k(dk_r, j + 2, i - S::DMA_INS);
     if (NEXT && i >= NM1) {
 #pragma unroll
       for (int e = 0; e < EPS; ++e) {
@@ -592,6 +601,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
           s_next[kb][r] = mask_score<CAUSAL>(s_next[kb][r], score_key(n1, kb, r, pp.g), pp.N, pp.qrow);
         mx = fmaxf(mx, s_next[kb][r]);
       }
+      asm volatile("" : "+v"(mx));  // the running maximum advances step by step
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -611,7 +621,7 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
 #define ITER(work)                                               \
   do {                                                           \
     work;                                                        \
-    wait_vmcnt<S::DMA_INS>(); /* all but K_{j+3} have landed */ \
+    wait_vmcnt<0>(); /* K_{j+2} has landed */                   \
     lds_barrier();                                               \
   } while (0)
   int j = 0;
@@ -635,9 +645,10 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
   // Tiles past this wave's rows: the same copies, conversion and waits.
   for (++j; j < n; ++j) {
     pp.issue_v(j + 1);
-    pp.issue_k(j + 3);
+    pp.issue_k(j + 2);
     wait_vmcnt<S::DMA_INS>();
     pp.template convert_v<IS_BF16>(j + 1);
+    wait_vmcnt<0>();
     lds_barrier();
   }
 #undef ITER
@@ -673,8 +684,11 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   pp.tid = tid;
   pp.qk = p.qk;
   pp.lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 1024);
-  pp.k_dma = dma_offset<D, false>(tid);
-  pp.v_dma = dma_offset<D, true>(tid);
+#pragma unroll
+  for (int c = 0; c < S::DMA_INS; ++c) {
+    pp.k_dma[c] = dma_offset<D, false>(tid) + c * 4096;
+    pp.v_dma[c] = dma_offset<D, true>(tid) + c * 4096;
+  }
   // This lane's query row; rows past N use row N-1's data and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
   pp.qrow = r0 + l32;
@@ -704,13 +718,12 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   st.neg_m = 0.f;
   st.l = 0.f;
 
-  // Prologue: V_0 and K_0..K_2 on their way; V_0 (converted) and S_0 once
+  // Prologue: V_0, K_0 and K_1 on their way; V_0 (converted) and S_0 once
   // V_0 and K_0 are in; K_1 in before iteration 0.
   pp.issue_v(0);
   pp.issue_k(0);
   pp.issue_k(1);
-  pp.issue_k(2);
-  wait_vmcnt<2 * S::DMA_INS>();  // V_0, K_0
+  wait_vmcnt<S::DMA_INS>();  // V_0, K_0
   pp.template convert_v<IS_BF16>(0);
   lds_barrier();
   f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
@@ -719,7 +732,7 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
     softmax_max<D, CAUSAL, true>(st, sa, 0, N, pp.qrow, pp.qk, g);
   else
     softmax_max<D, CAUSAL, false>(st, sa, 0, N, pp.qrow, pp.qk, g);
-  wait_vmcnt<S::DMA_INS>();  // K_1
+  wait_vmcnt<0>();  // K_1
   lds_barrier();
 
   run_wave<D, IS_BF16, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
