@@ -27,8 +27,9 @@
 //    A operand of QK^T, V through transposing reads (ds_read_b64_tr_b16)
 //    as the A operand of O^T. bf16 V is converted to fp16 in place in LDS.
 //  * each iteration is one stream of MFMAs (QK^T of the next tile, then P.V
-//    of this one) with the softmax work spread across it: on gfx950 a
-//    wave's vector instructions overlap its own MFMAs, not another wave's.
+//    of this one) with the softmax work spread across it: on gfx950 one wave
+//    cannot keep the MFMA pipe busy by itself, and two waves that each mix
+//    MFMAs with their own vector work hide that work best.
 //  * fp32 inputs use a separate kernel on v_mfma_f32_32x32x2_f32.
 #include <hip/hip_runtime.h>
 
@@ -124,11 +125,11 @@ __device__ __forceinline__ float sum_halves(float x) {
 // the header), each thread converting the 64 bytes its own copy brought in.
 // Tiles: d=128 uses 64 keys, d=64 uses 128.
 //
-// On gfx950 a wave's vector instructions run in the shadow of its own MFMAs,
-// not of another wave's, so each iteration is one stream of 2 x 16 MFMAs
-// (QK^T of tile j+1, then P_j V_j) with the softmax work of the tile -- the
-// exponentials of S_j and the row maximum of S_{j+1} -- spread over all of
-// its steps.
+// Each iteration is one stream of 2 x 16 MFMAs (QK^T of tile j+1, then
+// P_j V_j) with the softmax work of the tile -- the exponentials of S_j and
+// the row maximum of S_{j+1} -- spread over all of its steps: about four
+// vector instructions per MFMA run in its shadow when the two waves sharing
+// a SIMD both interleave this way.
 constexpr int kWaves16 = 4;
 constexpr int kThreads16 = kWaves16 * 64;
 constexpr int kBlockM16 = kWaves16 * 32;
