@@ -22,6 +22,7 @@
 #ifndef ATTN_FWD_ATTN_H
 #define ATTN_FWD_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -79,7 +80,8 @@ typedef enum {
  * Ownership: the caller allocates and owns all five buffers; the library
  * allocates nothing and keeps no per-call state, so concurrent calls on
  * different streams are safe. o and lse must not alias q, k or v (not
- * checked).
+ * checked). Buffers from a device allocator (256-byte aligned) are assumed;
+ * the kernels read and write 16-byte vectors.
  * Errors: every argument is validated before any HIP call is made, so the
  * error paths need no GPU. ATTN_ERR_HIP carries the raw hipError_t in
  * attn_last_hip_error().
@@ -87,6 +89,36 @@ typedef enum {
 attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
                      int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                      attn_dtype in_dtype, attn_dtype out_dtype, void *stream);
+
+/*
+ * attn_fwd_workspace_bytes -- bytes of device workspace attn_fwd_ws can use
+ * for this problem, 0 when it would use none.
+ *
+ * For bf16 inputs with N >= 8192 the bf16 -> fp16 conversion of V (see
+ * in_dtype above) runs once per element in a first pass that writes an
+ * fp16 copy of V, B*H*N*d*2 bytes, into the workspace, instead of once per
+ * 128-row query tile inside the attention kernel. Every other problem, and
+ * any invalid argument set, gives 0. No HIP call is made.
+ */
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype);
+
+/*
+ * attn_fwd_ws -- attn_fwd with a caller-owned device workspace.
+ *
+ * Arguments, validation, errors and results are those of attn_fwd; the
+ * results are bitwise identical to attn_fwd's. The workspace is used only
+ * when attn_fwd_workspace_bytes() > 0 for the problem, workspace_bytes is at
+ * least that, and workspace is non-NULL and 16-byte aligned; otherwise it is
+ * ignored and the call is exactly attn_fwd (no error is raised for it).
+ * The library never allocates, frees or retains the workspace. Its contents
+ * on entry do not matter and are unspecified afterwards, and it must not be
+ * used by other work until the enqueued work of this call has finished on
+ * `stream` (a second call on the same stream may reuse it).
+ */
+attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        attn_dtype in_dtype, attn_dtype out_dtype, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(attn_status s);

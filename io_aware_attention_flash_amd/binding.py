@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
           4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_fwd", "attn_status_string", "attn_abi_version", "attn_last_hip_error")
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_status_string",
+           "attn_abi_version", "attn_last_hip_error")
 
 _TORCH_TO_ATTN = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 _lib = None
@@ -41,6 +42,11 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd.restype = ctypes.c_int
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, vp]
+    lib.attn_fwd_ws.restype = ctypes.c_int
+    lib.attn_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                                ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_abi_version.restype = ctypes.c_int
@@ -64,13 +70,31 @@ def attn_fwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, scale,
                                    int(out_dtype), stream)
 
 
-def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=None):
+def attn_fwd_ws_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, scale,
+                    in_dtype, out_dtype, ws_ptr, ws_bytes, stream=None):
+    """Direct call of attn_fwd_ws (caller-owned workspace); returns the status."""
+    return load_library().attn_fwd_ws(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, int(B), int(H), int(N),
+                                      int(d), int(bool(causal)), float(scale), int(in_dtype),
+                                      int(out_dtype), ws_ptr, int(ws_bytes), stream)
+
+
+def workspace_bytes(B, H, N, d, in_dtype):
+    """Bytes of device workspace attn_fwd_ws can use for this problem (0: none)."""
+    return int(load_library().attn_fwd_workspace_bytes(int(B), int(H), int(N), int(d),
+                                                       int(in_dtype)))
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=None,
+             workspace=None):
     """Attention forward of [B, H, N, d] tensors on the current HIP stream.
 
     scale defaults to 1/sqrt(d); out_dtype defaults to the input dtype
     (torch.float32 is also accepted for bf16/fp16 inputs). Returns (o, lse)
     with lse [B, H, N] fp32 natural-log logsumexp. Preallocated `out`/`lse`
-    may be passed to avoid allocation.
+    may be passed to avoid allocation. When the problem can use a device
+    workspace (long bf16 sequences), a uint8 tensor of at least
+    workspace_bytes(...) bytes may be passed as `workspace`; otherwise one is
+    taken from torch's allocator for the call.
     """
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must all be [B, H, N, d] of one shape")
@@ -97,9 +121,22 @@ def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=No
     if out_dtype not in _TORCH_TO_ATTN:
         raise ValueError("unsupported out_dtype %s" % out_dtype)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, N, d, causal, scale, _TORCH_TO_ATTN[q.dtype],
-                      _TORCH_TO_ATTN[out_dtype], stream)
+    need = workspace_bytes(B, H, N, d, _TORCH_TO_ATTN[q.dtype])
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if not (workspace.is_cuda and workspace.device == q.device and workspace.is_contiguous()
+                and workspace.numel() * workspace.element_size() >= need):
+            raise ValueError("workspace must be a contiguous tensor of at least %d bytes on q's "
+                             "device" % need)
+        st = attn_fwd_ws_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, N, d, causal, scale, _TORCH_TO_ATTN[q.dtype],
+                             _TORCH_TO_ATTN[out_dtype], workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), stream)
+    else:
+        st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, causal, scale, _TORCH_TO_ATTN[q.dtype],
+                          _TORCH_TO_ATTN[out_dtype], stream)
     if st != 0:
         msg = status_string(st)
         if st == 5:

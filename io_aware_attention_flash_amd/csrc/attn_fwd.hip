@@ -435,9 +435,9 @@ struct Pipe16 {
   __device__ __forceinline__ u32x4 *v_slot(int t, int c) const {
     return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * 2048 + tid * 8);
   }
-  template <bool IS_BF16>
+  template <bool CONV_V>
   __device__ __forceinline__ void convert_v(int t) const {
-    if (!IS_BF16 || t >= n_tiles) return;
+    if (!CONV_V || t >= n_tiles) return;
 #pragma unroll
     for (int c = 0; c < Shape16<D>::DMA_INS; ++c) *v_slot(t, c) = to_f16(*v_slot(t, c));
   }
@@ -503,7 +503,7 @@ struct PairPlan {
 // slot per two steps (load, then convert and store). VPAR is j's parity
 // when known at compile time (-1 otherwise), which makes the V stage
 // addresses constants.
-template <int D, bool IS_BF16, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
+template <int D, bool IS_BF16, bool CONV_V, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
 __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
                                           int j, f32x16 (&s)[Shape16<D>::NKB],
                                           f32x16 (&s_next)[Shape16<D>::NKB]) {
@@ -574,7 +574,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
         asm volatile("" : "+v"(lsum) : "v"(h));
       }
     }
-    if (IS_BF16 && i >= CW && i <= CW + 2 * NI) {
+    if (CONV_V && i >= CW && i <= CW + 2 * NI) {
       // Slot c is read at step CW + 2c; its first two dwords are converted
       // one step later, the other two and the store one more later. Past
       // the last tile the copy brought zeros, which convert harmlessly.
@@ -613,7 +613,7 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
 // All iterations of one wave. nw: key tiles this wave visits, nfw: leading
 // tiles it needs no mask for; the workgroup runs pp.n_tiles iterations, each
 // ending with the copies' wait, the bf16 conversion and a barrier.
-template <int D, bool IS_BF16, bool CAUSAL>
+template <int D, bool IS_BF16, bool CONV_V, bool CAUSAL>
 __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
                                          f32x16 (&sa)[Shape16<D>::NKB],
                                          f32x16 (&sb)[Shape16<D>::NKB], int nw, int nfw) {
@@ -628,34 +628,36 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
   int j = 0;
   const int n_a = max(min(nfw, nw) - 1, 0);  // tiles j < n_a have an unmasked successor
   for (; j + 2 <= n_a; j += 2) {
-    ITER((iteration<D, IS_BF16, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
-    ITER((iteration<D, IS_BF16, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
+    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
   }
   if (j < n_a) {  // odd count of unmasked successors
-    ITER((iteration<D, IS_BF16, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
     ++j;
   }
   for (; j < nw - 1; ++j) {
-    ITER((iteration<D, IS_BF16, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
   }
-  ITER((iteration<D, IS_BF16, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
+  ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
   // Tiles past this wave's rows: the same copies, conversion and waits.
   for (++j; j < n; ++j) {
     pp.issue_v(j + 1);
     pp.issue_k(j + 2);
     wait_vmcnt<S::DMA_INS>();
-    pp.template convert_v<IS_BF16>(j + 1);
+    pp.template convert_v<CONV_V>(j + 1);
     wait_vmcnt<0>();
     lds_barrier();
   }
 #undef ITER
 }
 
-template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32>
+// CONV_V: V arrives as bf16 and is converted in LDS; without it V is fp16
+// already (fp16 inputs, or bf16 inputs whose V a first pass converted).
+template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
 __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
@@ -725,7 +727,7 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   pp.issue_k(0);
   pp.issue_k(1);
   wait_vmcnt<S::DMA_INS>();  // V_0, K_0
-  pp.template convert_v<IS_BF16>(0);
+  pp.template convert_v<CONV_V>(0);
   lds_barrier();
   f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
   qk_tile<D, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
@@ -736,7 +738,7 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   wait_vmcnt<0>();  // K_1
   lds_barrier();
 
-  run_wave<D, IS_BF16, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
+  run_wave<D, IS_BF16, CONV_V, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
 
   // Copies issued for tiles past the end (empty byte ranges) retire before
   // the workgroup's LDS can be handed to another one.
@@ -890,20 +892,55 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32(FwdParams p) {
 }
 
 // --------------------------------------------------------------------------
+// First pass for long bf16 sequences: V -> fp16 into a workspace, once per
+// element, instead of once per query tile inside the attention kernel (the
+// same rounding: exact for |v| in [2^-14, 65504]). Eight values per thread
+// per step of a grid-stride loop; n8 counts groups of eight.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void v_to_f16(const u32x4 *src, u32x4 *dst, int64_t n8) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const u32x4 x = src[i];
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = pack_f16(bf16_lo_to_f32(x[e]), bf16_hi_to_f32(x[e]));
+    dst[i] = y;
+  }
+}
+constexpr int kPrepassBlocks = 8192;
+// The first pass costs about as much as the in-LDS conversion saves at
+// N = 4096 (causal) and pays off from about twice that: kernel time grows
+// with N^2, the pass with N.
+constexpr int64_t kPrepassMinN = 8192;
+
+// --------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.
 // --------------------------------------------------------------------------
 typedef void (*KernelFn)(FwdParams);
 
 template <int D, bool IS_BF16, bool CAUSAL>
-KernelFn pick16(bool out_f32) {
-  return out_f32 ? attn_fwd_16<D, IS_BF16, CAUSAL, true> : attn_fwd_16<D, IS_BF16, CAUSAL, false>;
+KernelFn pick16(bool out_f32, bool conv_v) {
+  if (IS_BF16 && conv_v)
+    return out_f32 ? attn_fwd_16<D, IS_BF16, CAUSAL, true, IS_BF16>
+                   : attn_fwd_16<D, IS_BF16, CAUSAL, false, IS_BF16>;
+  return out_f32 ? attn_fwd_16<D, IS_BF16, CAUSAL, true, false>
+                 : attn_fwd_16<D, IS_BF16, CAUSAL, false, false>;
 }
 
 template <int D>
-KernelFn pick_d(attn_dtype in, bool out_f32, bool causal) {
+KernelFn pick_d(attn_dtype in, bool out_f32, bool causal, bool conv_v) {
   if (in == ATTN_F32) return causal ? attn_fwd_f32<D, true> : attn_fwd_f32<D, false>;
-  if (in == ATTN_BF16) return causal ? pick16<D, true, true>(out_f32) : pick16<D, true, false>(out_f32);
-  return causal ? pick16<D, false, true>(out_f32) : pick16<D, false, false>(out_f32);
+  if (in == ATTN_BF16)
+    return causal ? pick16<D, true, true>(out_f32, conv_v) : pick16<D, true, false>(out_f32, conv_v);
+  return causal ? pick16<D, false, true>(out_f32, false) : pick16<D, false, false>(out_f32, false);
+}
+
+// Bytes of the fp16 copy of V the first pass writes, or 0 when the problem
+// does not take the first pass (or is invalid).
+size_t prepass_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype) {
+  if (in_dtype != ATTN_BF16 || N < kPrepassMinN || (d != 64 && d != 128)) return 0;
+  if (B < 1 || H < 1 || N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return 0;
+  return (size_t)(B * H) * (size_t)N * (size_t)d * 2;
 }
 
 thread_local int g_last_hip_error = 0;
@@ -928,9 +965,10 @@ const char *attn_status_string(attn_status s) {
   return "unknown status";
 }
 
-attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
-                     int64_t H, int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
-                     attn_dtype out_dtype, void *stream) {
+static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                 float scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
   // Validation first: no HIP call happens before every argument is checked.
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
@@ -964,17 +1002,55 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
   double qk = (double)scale * 1.4426950408889634;
   p.qk = qk < (double)FLT_MIN ? FLT_MIN : (float)qk;
 
+  // The first pass runs when the problem takes it and the workspace can hold
+  // its output (16-byte aligned); otherwise the kernel converts V in LDS.
+  // Both give the same bits.
+  const size_t need = prepass_bytes(B, H, N, d, in_dtype);
+  const bool prepass = need > 0 && workspace != nullptr && workspace_bytes >= need &&
+                       (reinterpret_cast<uintptr_t>(workspace) & 15) == 0;
   const bool out_f32 = out_dtype == ATTN_F32;
-  KernelFn fn = d == 64 ? pick_d<64>(in_dtype, out_f32, causal != 0)
-                        : pick_d<128>(in_dtype, out_f32, causal != 0);
-  void *args[] = {&p};
-  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
-                                         dim3(threads), args, 0, (hipStream_t)stream);
+  KernelFn fn = d == 64 ? pick_d<64>(in_dtype, out_f32, causal != 0, !prepass)
+                        : pick_d<128>(in_dtype, out_f32, causal != 0, !prepass);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t err = hipSuccess;
+  if (prepass) {
+    int64_t n8 = (int64_t)(need / 16);
+    const int64_t blocks = (n8 + 255) / 256 < kPrepassBlocks ? (n8 + 255) / 256 : kPrepassBlocks;
+    const void *src = v;
+    void *cargs[] = {&src, &workspace, &n8};
+    err = hipLaunchKernel(reinterpret_cast<const void *>(v_to_f16), dim3((unsigned)blocks),
+                          dim3(256), cargs, 0, st);
+    p.v = workspace;
+  }
+  if (err == hipSuccess) {
+    void *args[] = {&p};
+    err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid), dim3(threads),
+                          args, 0, st);
+  }
   if (err != hipSuccess) {
     g_last_hip_error = (int)err;
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float *lse, int64_t B,
+                     int64_t H, int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
+                     attn_dtype out_dtype, void *stream) {
+  return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
+                       stream);
+}
+
+size_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype) {
+  return prepass_bytes(B, H, N, d, in_dtype);
+}
+
+attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, float *lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                        attn_dtype in_dtype, attn_dtype out_dtype, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -103,3 +103,35 @@ def test_package_import_loads_nothing():
     import io_aware_attention_flash_amd as pkg
     assert callable(pkg.attn_fwd)
     assert ctypes is not None
+
+
+@pytest.mark.parametrize("B,H,N,d,dt,want", [
+    (1, 1, 8192, 128, 2, 8192 * 128 * 2),
+    (2, 3, 8192, 64, 2, 2 * 3 * 8192 * 64 * 2),
+    (1, 16, 16384, 128, 2, 16 * 16384 * 128 * 2),
+    (1, 1, 8191, 128, 2, 0),          # shorter sequences convert inside the kernel
+    (1, 1, 8192, 128, 1, 0),          # fp16 V needs no conversion
+    (1, 1, 8192, 128, 0, 0),
+    (1, 1, 8192, 96, 2, 0),           # invalid arguments give 0
+    (0, 1, 8192, 128, 2, 0),
+    (1, 1, (1 << 24) + 1, 128, 2, 0),
+])
+def test_workspace_bytes(lib, B, H, N, d, dt, want):
+    assert binding.workspace_bytes(B, H, N, d, dt) == want
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), 1), (dict(lse=0), 1), (dict(N=0), 2), (dict(d=96), 3),
+    (dict(i=2, o_t=1), 3), (dict(scale=float("nan")), 4),
+])
+def test_workspace_entry_validates_first(lib, args, code):
+    """attn_fwd_ws validates exactly like attn_fwd, before any HIP call,
+    with or without a workspace."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=8192, d=128, causal=0, scale=0.125,
+             i=2, o_t=0)
+    a.update(args)
+    for ws, nbytes in ((None, 0), (P, 1 << 30)):
+        st = binding.attn_fwd_ws_raw(a["q"] or None, a["k"] or None, a["v"] or None,
+                                     a["o"] or None, a["lse"] or None, a["B"], a["H"], a["N"],
+                                     a["d"], a["causal"], a["scale"], a["i"], a["o_t"], ws, nbytes)
+        assert st == code, (args, ws, st)

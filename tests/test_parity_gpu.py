@@ -229,3 +229,54 @@ def test_out_and_lse_buffers_untouched_outside():
     torch.cuda.synchronize()
     assert bool((big[:1024] == 7.0).all() and (big[1024 + n:] == 7.0).all())
     assert bool((lbig[:1024] == 7.0).all() and (lbig[1024 + B * H * N:] == 7.0).all())
+
+
+# ------------------------------------------- the workspace (first-pass) path
+WS_CASES = [
+    # (B, H, N, d, causal): long bf16 sequences take the first pass
+    (1, 2, 8192, 128, True),
+    (1, 1, 8200, 64, False),
+]
+
+
+def _raw(q, k, v, causal, scale, ws=None, ws_bytes=0):
+    B, H, N, d = q.shape
+    o = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+            causal, scale, binding.ATTN_BF16, binding.ATTN_F32)
+    if ws is None:
+        st = binding.attn_fwd_raw(*args, stream)
+    else:
+        st = binding.attn_fwd_ws_raw(*args, ws, ws_bytes, stream)
+    assert st == 0, binding.status_string(st)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("case", WS_CASES, ids=lambda c: "B%dH%dN%dd%d_%s" % (
+    c[0], c[1], c[2], c[3], "causal" if c[4] else "full"))
+def test_workspace_path(case):
+    """attn_fwd_ws gives attn_fwd's bits whether or not it uses the
+    workspace; the workspace then holds V in fp16 (torch's rounding) and
+    nothing past it is written; the results meet the oracle."""
+    B, H, N, d, causal = case
+    _say("workspace case", case)
+    qc, kc, vc = make_qkv(B, H, N, d, "bf16", 1.0, seed=11)
+    q, k, v = qc.cuda(), kc.cuda(), vc.cuda()
+    sc = _scale(d)
+    need = binding.workspace_bytes(B, H, N, d, binding.ATTN_BF16)
+    assert need == B * H * N * d * 2
+    base_o, base_l = _raw(q, k, v, causal, sc)
+    ws = torch.full((need + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    o, lse = _raw(q, k, v, causal, sc, ws.data_ptr(), need)
+    assert torch.equal(o, base_o) and torch.equal(lse, base_l)
+    assert torch.equal(ws[:need].view(torch.float16).view(v.shape), v.to(torch.float16))
+    assert bool((ws[need:] == 0x5A).all())
+    # Too small or misaligned: ignored, same bits.
+    for ptr, nbytes in ((ws.data_ptr(), need - 16), (ws.data_ptr() + 8, need)):
+        o2, l2 = _raw(q, k, v, causal, sc, ptr, nbytes)
+        assert torch.equal(o2, base_o) and torch.equal(l2, base_l)
+    ref_o, ref_l = oracle.attn_oracle(qc, kc, vc, causal=causal, scale=sc)
+    check_close(o.cpu().numpy(), lse.cpu().numpy(), ref_o, ref_l, "workspace " + str(case))
