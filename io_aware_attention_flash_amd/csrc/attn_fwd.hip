@@ -12,7 +12,8 @@
 // back to the natural log ("Kernel 4", notes on exp2 and the saved L).
 //
 // gfx950 mapping (our design, not the page's):
-//  * a workgroup is 4 wave64s and 128 query rows; each wave owns 32 rows.
+//  * each wave owns 32 query rows; a workgroup is 8 waves (256 rows) for
+//    d=128 and 4 waves (128 rows) for d=64.
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: with the 32x32 output
 //    layout each lane then holds the scores of ONE query row (lane & 31) for
 //    16 keys per 32-key block, so the row maximum is an in-lane max plus one
@@ -23,7 +24,7 @@
 //    fp16), and the O^T accumulator has the same row-per-lane layout, so
 //    rescaling by alpha is a per-lane scalar multiply.
 //  * K and V tiles are copied from memory straight into LDS rings
-//    (buffer_load ... lds) and read from there by all four waves: K as the
+//    (buffer_load ... lds) and read from there by all the waves: K as the
 //    A operand of QK^T, V through transposing reads (ds_read_b64_tr_b16)
 //    as the A operand of O^T. bf16 V is converted to fp16 in place in LDS.
 //  * each iteration is one stream of MFMAs (QK^T of the next tile, then P.V
@@ -113,16 +114,19 @@ __device__ __forceinline__ float sum_halves(float x) {
 // --------------------------------------------------------------------------
 // bf16 / fp16 kernel
 // --------------------------------------------------------------------------
-// A workgroup is 4 wave64s and 128 query rows (32 per wave); two
-// workgroups share a CU, so the two waves on a SIMD never wait on each
-// other. K and V tiles go from global memory straight into LDS
-// (buffer_load ... lds, no register staging): K through a ring of three
-// stages (fetched two iterations before use), V through two (one iteration
-// before). Both stay row-major; 16-byte chunks are XOR-swizzled per row so
+// Each wave owns 32 query rows. For d=128 a workgroup is 8 waves (256 rows,
+// one workgroup per CU, two of its waves per SIMD): every K/V tile copied
+// into LDS, and every bf16 V tile converted there, then serves twice as many
+// rows as with 4-wave workgroups, which measured 5-7% faster despite the
+// two waves of a SIMD meeting at the same barriers. For d=64 (128-key
+// tiles) a workgroup is 4 waves and two share a CU, which measured faster
+// there. K and V tiles go from global memory straight into LDS
+// (buffer_load ... lds, no register staging), each through a ring of two
+// stages (fetched one iteration before use). Both stay row-major; 16-byte chunks are XOR-swizzled per row so
 // the lane-contiguous DMA writes, the K operand reads and the transposing V
 // reads (ds_read_b64_tr_b16) are free of bank conflicts or nearly so. bf16 V
 // is converted to fp16 in place in LDS (the P.V product runs in fp16, see
-// the header), each thread converting the 64 bytes its own copy brought in.
+// the header), each thread converting the bytes its own copy brought in.
 // Tiles: d=128 uses 64 keys, d=64 uses 128.
 //
 // Each iteration is one stream of 2 x 16 MFMAs (QK^T of tile j+1, then
@@ -130,25 +134,27 @@ __device__ __forceinline__ float sum_halves(float x) {
 // the row maximum of S_{j+1} -- spread over all of its steps: about four
 // vector instructions per MFMA run in its shadow when the two waves sharing
 // a SIMD both interleave this way.
-constexpr int kWaves16 = 4;
-constexpr int kThreads16 = kWaves16 * 64;
-constexpr int kBlockM16 = kWaves16 * 32;
 constexpr int kKStages = 2;
 constexpr int kVStages = 2;
 
 template <int D>
 struct Shape16 {
+  static constexpr int WAVES = (D == 128) ? 8 : 4;       // per workgroup
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BLOCK_M = WAVES * 32;             // query rows per workgroup
+  static constexpr int WG_PER_CU = 8 / WAVES;            // two waves per SIMD
   static constexpr int BN = (D == 128) ? 64 : 128;
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int TILE_ELEMS = BN * D;              // one K or V stage
   static constexpr int TILE_BYTES = TILE_ELEMS * 2;
-  static constexpr int DMA_INS = BN * CPR / kThreads16;  // DMA instructions per thread and tile
+  static constexpr int DMA_INS = BN * CPR / THREADS;     // DMA instructions per thread and tile
+  static constexpr int INS_BYTES = THREADS * 16;         // bytes one DMA instruction moves
   static constexpr int NKB = BN / 32;                    // 32-key blocks per tile
   static constexpr int NCB = D / 32;                     // 32-column blocks of O^T
   static constexpr int NKC = D / 16;                     // 16-wide QK^T k-chunks
   static constexpr int NT = BN / 16;                     // 16-key PV k-chunks
-  static_assert(DMA_INS * kThreads16 == BN * CPR, "DMA covers the tile");
-  static_assert(DMA_INS * kThreads16 * 16 == TILE_BYTES, "each DMA instruction moves 4 KiB");
+  static_assert(DMA_INS * THREADS == BN * CPR, "DMA covers the tile");
+  static_assert(DMA_INS * INS_BYTES == TILE_BYTES, "each DMA instruction moves 16 bytes a thread");
 };
 
 // Rows of the online softmax are rescaled only when their maximum grows by
@@ -215,11 +221,11 @@ __device__ __forceinline__ void dma16_to_lds(u32x4 rsrc, uint32_t lds_byte, uint
 }
 
 // DMA of one K or V tile into an LDS stage. Instruction c fills the 16-byte
-// slots c*256 + tid: slot s holds physical chunk s % CPR of tile row s / CPR,
-// i.e. logical chunk (s % CPR) ^ swz(row). Instruction c covers the c-th
-// 4 KiB of the tile, a whole number of swizzle periods, so its lane offset is
-// that of c = 0 plus 4096 c. The offset stays in a VGPR (the descriptor's
-// range check applies to it, not to an SGPR offset).
+// slots c*THREADS + tid: slot s holds physical chunk s % CPR of tile row
+// s / CPR, i.e. logical chunk (s % CPR) ^ swz(row). Instruction c covers the
+// c-th INS_BYTES of the tile, a whole number of swizzle periods, so its lane
+// offset is that of c = 0 plus c * INS_BYTES. The offset stays in a VGPR
+// (the descriptor's range check applies to it, not to an SGPR offset).
 template <int D, bool IS_V>
 __device__ __forceinline__ uint32_t dma_offset(int tid) {
   constexpr int CPR = Shape16<D>::CPR;
@@ -413,11 +419,11 @@ struct Pipe16 {
   // Instruction c of the copy of K_t / V_t (descriptor r).
   __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (t & 1) * TB + c * 4096, k_dma[c]);
+    dma16_to_lds(r, lds_wave + (t & 1) * TB + c * Shape16<D>::INS_BYTES, k_dma[c]);
   }
   __device__ __forceinline__ void copy_v(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * 4096, v_dma[c]);
+    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * Shape16<D>::INS_BYTES, v_dma[c]);
   }
   __device__ __forceinline__ void issue_k(int t) const {
     const u32x4 r = k_rsrc(t);
@@ -433,7 +439,7 @@ struct Pipe16 {
   // the copy has landed (this wave's vmcnt wait), the thread converts them
   // from bf16 to fp16 in place.
   __device__ __forceinline__ u32x4 *v_slot(int t, int c) const {
-    return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * 2048 + tid * 8);
+    return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * (Shape16<D>::INS_BYTES / 2) + tid * 8);
   }
   template <bool CONV_V>
   __device__ __forceinline__ void convert_v(int t) const {
@@ -658,7 +664,7 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
 // CONV_V: V arrives as bf16 and is converted in LDS; without it V is fp16
 // already (fp16 inputs, or bf16 inputs whose V a first pass converted).
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
-__global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
+__global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
   constexpr int NCB = S::NCB;
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   int bh, qt;
   work_item<CAUSAL>(p, bh, qt);
   const int N = p.N;
-  const int m0 = qt * kBlockM16;
+  const int m0 = qt * S::BLOCK_M;
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + head;
 
@@ -689,8 +695,8 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   pp.lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 1024);
 #pragma unroll
   for (int c = 0; c < S::DMA_INS; ++c) {
-    pp.k_dma[c] = dma_offset<D, false>(tid) + c * 4096;
-    pp.v_dma[c] = dma_offset<D, true>(tid) + c * 4096;
+    pp.k_dma[c] = dma_offset<D, false>(tid) + c * S::INS_BYTES;
+    pp.v_dma[c] = dma_offset<D, true>(tid) + c * S::INS_BYTES;
   }
   // This lane's query row; rows past N use row N-1's data and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(kThreads16, 2) void attn_fwd_16(FwdParams p) {
   // wave (compute). Causal: only tiles holding some key <= the last row.
   // Tiles [0, nfw) need no mask for this wave.
   const int n_all = (N + BN - 1) / BN;
-  const int n_tiles = CAUSAL ? min(n_all, (m0 + kBlockM16 + BN - 1) / BN) : n_all;
+  const int n_tiles = CAUSAL ? min(n_all, (m0 + S::BLOCK_M + BN - 1) / BN) : n_all;
   const int nw = CAUSAL ? min(n_all, (r0 + 32 + BN - 1) / BN) : n_all;
   int nfw = N / BN;
   if (CAUSAL) nfw = min(nfw, (r0 + 1) / BN);
@@ -982,8 +988,8 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
   // Query rows per workgroup and threads per workgroup of the chosen kernel.
   const bool f32_path = in_dtype == ATTN_F32;
-  const int64_t block_m = f32_path ? kBlockM : kBlockM16;
-  const unsigned threads = f32_path ? kThreads : kThreads16;
+  const int64_t block_m = f32_path ? kBlockM : d == 64 ? Shape16<64>::BLOCK_M : Shape16<128>::BLOCK_M;
+  const unsigned threads = f32_path ? kThreads : d == 64 ? Shape16<64>::THREADS : Shape16<128>::THREADS;
   const int64_t nq = (N + block_m - 1) / block_m;
   const int64_t grid = nq * B * H;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;

@@ -75,7 +75,7 @@ SMALL_CASES = [
     (1, 2, 517, 128, "bf16", True, 3.0),
     (1, 2, 640, 64, "f16", True, 1.0),
     (1, 1, 1000, 128, "bf16", False, 3.0),
-    # tile edges: d=128 uses 64-key tiles, d=64 128-key tiles; 128 query rows per workgroup
+    # tile edges: d=128 uses 64-key tiles, d=64 128-key tiles
     (1, 2, 64, 128, "f16", False, 1.0),
     (1, 2, 128, 64, "bf16", True, 1.0),
     (1, 2, 129, 64, "bf16", False, 1.0),
@@ -83,6 +83,12 @@ SMALL_CASES = [
     (1, 1, 192, 128, "f16", True, 1.0),
     (1, 1, 385, 64, "f16", True, 2.0),
     (3, 5, 97, 128, "bf16", True, 1.0),
+    # d=128 workgroups hold 256 query rows, d=64 ones 128
+    (1, 1, 255, 128, "bf16", True, 1.0),
+    (1, 1, 256, 128, "f16", True, 1.0),
+    (1, 2, 257, 128, "bf16", False, 1.0),
+    (1, 1, 511, 128, "f16", False, 1.0),
+    (2, 1, 513, 128, "bf16", True, 2.0),
 ]
 
 
