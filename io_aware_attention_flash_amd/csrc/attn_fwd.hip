@@ -661,6 +661,23 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
 #undef ITER
 }
 
+// Row-major staging of one wave's 32 x D block of O in LDS for the
+// epilogue: E bytes per element, rows of ROWB bytes (a whole row of O, or a
+// 256-byte part of it when longer: PASSES parts), CPR 16-byte chunks per row,
+// XOR-swizzled by row so the row-per-lane writes and the row-by-row reads
+// spread over the banks; one wave instruction reads RPI rows.
+template <int D, int E_>
+struct OutStage {
+  static constexpr int E = E_;
+  static constexpr int ROWB = D * E > 256 ? 256 : D * E;
+  static constexpr int PASSES = D * E / ROWB;
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RPI = 64 / CPR;
+  static constexpr int COLS = ROWB / E;
+  static constexpr int WAVE_BYTES = 32 * ROWB;
+  __device__ static constexpr int swz(int row) { return row & (CPR - 1); }
+};
+
 // CONV_V: V arrives as bf16 and is converted in LDS; without it V is fp16
 // already (fp16 inputs, or bf16 inputs whose V a first pass converted).
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
@@ -754,29 +771,53 @@ __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void at
   const float l_tot = sum_halves(st.l);
   const float l_safe = l_tot > 0.f ? l_tot : 1.f;
   const float inv = 1.0f / l_safe;
-  const int qrow = pp.qrow;
-  if (qrow < N) {
-    if (g == 0) p.lse[(size_t)bh * N + qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
-    const size_t orow = head + (size_t)qrow * D;
+  if (pp.qrow < N && g == 0)
+    p.lse[(size_t)bh * N + pp.qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
+  // O leaves through LDS. A lane holds one row, so stores straight from the
+  // accumulators would touch 64 rows (64 cache lines) per instruction; staged
+  // row-major, each store instruction writes whole lines. Once every wave has
+  // passed this barrier none reads the K/V stages any more (and no copy is in
+  // flight), and each wave reuses its own slice of that memory.
+  lds_barrier();
+  using OS = OutStage<D, OUT_F32 ? 4 : 2>;
+  static_assert(S::WAVES * OS::WAVE_BYTES <= (kKStages + kVStages) * S::TILE_BYTES, "staging fits");
+  uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + wave * OS::WAVE_BYTES;
+  uint8_t *obase = static_cast<uint8_t *>(p.o) + (head + (size_t)r0 * D) * OS::E;
+#pragma unroll
+  for (int ps = 0; ps < OS::PASSES; ++ps) {
+    // This lane's row l32: 4-column pieces at 32cb + 8r4 + 4g.
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int c0 = cb * 32 + r4 * 8 + g * 4;
+        const int col = cb * 32 + r4 * 8 + g * 4 - ps * OS::COLS;
+        if (col < 0 || col >= OS::COLS) continue;
+        const int byte = col * OS::E;
+        uint8_t *dst = stage + l32 * OS::ROWB + (((byte >> 4) ^ OS::swz(l32)) << 4) + (byte & 15);
         const float o0 = st.acc[cb][4 * r4 + 0] * inv, o1 = st.acc[cb][4 * r4 + 1] * inv;
         const float o2 = st.acc[cb][4 * r4 + 2] * inv, o3 = st.acc[cb][4 * r4 + 3] * inv;
         if (OUT_F32) {
-          *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + orow + c0) = f32x4{o0, o1, o2, o3};
+          *reinterpret_cast<f32x4 *>(dst) = f32x4{o0, o1, o2, o3};
         } else if (IS_BF16) {
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-          const bf16x4 h = {(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
-          *reinterpret_cast<bf16x4 *>(static_cast<uint16_t *>(p.o) + orow + c0) = h;
+          *reinterpret_cast<bf16x4 *>(dst) = bf16x4{(__bf16)o0, (__bf16)o1, (__bf16)o2, (__bf16)o3};
         } else {
           typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-          const f16x4 h = {(_Float16)o0, (_Float16)o1, (_Float16)o2, (_Float16)o3};
-          *reinterpret_cast<f16x4 *>(static_cast<uint16_t *>(p.o) + orow + c0) = h;
+          *reinterpret_cast<f16x4 *>(dst) =
+              f16x4{(_Float16)o0, (_Float16)o1, (_Float16)o2, (_Float16)o3};
         }
       }
+    __builtin_amdgcn_wave_barrier();
+    // Read back by rows: lane = (row within the group, 16-byte chunk).
+#pragma unroll
+    for (int k = 0; k < 32 / OS::RPI; ++k) {
+      const int row = k * OS::RPI + lane / OS::CPR, c = lane % OS::CPR;
+      const u32x4 val =
+          *reinterpret_cast<const u32x4 *>(stage + row * OS::ROWB + ((c ^ OS::swz(row)) << 4));
+      if (r0 + row < N)
+        *reinterpret_cast<u32x4 *>(obase + (size_t)row * D * OS::E + ps * OS::ROWB + c * 16) = val;
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
