@@ -680,21 +680,23 @@ struct OutStage {
 
 // CONV_V: V arrives as bf16 and is converted in LDS; without it V is fp16
 // already (fp16 inputs, or bf16 inputs whose V a first pass converted).
+// One query tile (BLOCK_M rows of head bh) from the load of Q to the stores
+// of O and LSE.
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
-__global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
+__device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int bh, int qt) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
   constexpr int NCB = S::NCB;
   constexpr int NKC = S::NKC;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[(kKStages + kVStages) * S::TILE_ELEMS];
 
-  const int tid = threadIdx.x;
+  // Opaque per call: the lane addresses derived from it are recomputed for
+  // each tile instead of being held in registers across a workgroup's tiles.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  int bh, qt;
-  work_item<CAUSAL>(p, bh, qt);
   const int N = p.N;
   const int m0 = qt * S::BLOCK_M;
   const size_t head = (size_t)bh * (size_t)N * D;
@@ -818,6 +820,33 @@ __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void at
         *reinterpret_cast<u32x4 *>(obase + (size_t)row * D * OS::E + ps * OS::ROWB + c * 16) = val;
     }
     __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Causal query tiles differ in length (tile t visits about t+1 key tiles),
+// and with one tile per workgroup the last workgroups to finish leave CUs
+// idle. A causal workgroup therefore takes tile nq-1-i and then tile i: all
+// pairs are equally long (the middle tile of an odd count runs alone, last).
+// Workgroup ids run pair-major, head-minor, so the 8 XCDs (round-robin over
+// ids) each keep the same heads.
+template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
+__global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
+  using S = Shape16<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[(kKStages + kVStages) * S::TILE_ELEMS];
+  const int w = blockIdx.x;
+  const int t = w / p.BH;
+  const int bh = w - t * p.BH;
+  if (!CAUSAL) {
+    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t);
+    return;
+  }
+  const int qa = p.nq - 1 - t, qb = t;
+  const int n_items = qb < qa ? 2 : 1;
+#pragma unroll 1
+  for (int k = 0; k < n_items; ++k) {
+    // The second tile's copies reuse the LDS the first one's epilogue read.
+    if (k > 0) lds_barrier();
+    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb);
   }
 }
 
@@ -1032,7 +1061,8 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   const int64_t block_m = f32_path ? kBlockM : d == 64 ? Shape16<64>::BLOCK_M : Shape16<128>::BLOCK_M;
   const unsigned threads = f32_path ? kThreads : d == 64 ? Shape16<64>::THREADS : Shape16<128>::THREADS;
   const int64_t nq = (N + block_m - 1) / block_m;
-  const int64_t grid = nq * B * H;
+  // Causal bf16/fp16 workgroups take two query tiles each (long + short).
+  const int64_t grid = (causal && !f32_path ? (nq + 1) / 2 : nq) * B * H;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
 
   FwdParams p;
