@@ -149,6 +149,17 @@ struct Shape16 {
   static constexpr int TILE_BYTES = TILE_ELEMS * 2;
   static constexpr int DMA_INS = BN * CPR / THREADS;     // DMA instructions per thread and tile
   static constexpr int INS_BYTES = THREADS * 16;         // bytes one DMA instruction moves
+  static constexpr int Q_INS = BLOCK_M * D * 2 / INS_BYTES;  // DMA instructions for the Q tile
+  static constexpr int RING_ELEMS = 4 * TILE_ELEMS;      // K stages 0..1, V stages 0..1
+  static_assert(kKStages + kVStages == 4, "ring size");
+  // d=128 (one workgroup per CU) stages O for the epilogue in LDS of its own,
+  // in 128-byte rows, so a workgroup can copy its next tile's first K/V tiles
+  // and Q into the ring while it writes out O; d=64 (two workgroups per CU)
+  // has no room left and stages in the ring, in 256-byte rows.
+  static constexpr bool OWN_STAGE = (D == 128);
+  static constexpr int STAGE_ROWB = OWN_STAGE ? 128 : 256;
+  static constexpr int STAGE_ELEMS = OWN_STAGE ? WAVES * 32 * STAGE_ROWB / 2 : 0;
+  static constexpr int LDS_ELEMS = RING_ELEMS + BLOCK_M * D + STAGE_ELEMS;
   static constexpr int NKB = BN / 32;                    // 32-key blocks per tile
   static constexpr int NCB = D / 32;                     // 32-column blocks of O^T
   static constexpr int NKC = D / 16;                     // 16-wide QK^T k-chunks
@@ -313,16 +324,23 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t *vst, const LaneAddr<D> &
   return u32x4{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// S^T[kb] = K_kb Q^T for one tile (used once, before the pipelined loop).
+// S^T[kb] = K_kb Q^T for one tile (once per query tile, before the
+// pipelined loop), the K operands read three steps ahead of their MFMAs.
 template <int D, bool IS_BF16>
 __device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *kst,
                                         const LaneAddr<D> &la) {
   using S = Shape16<D>;
+  constexpr int NM = S::NKB * S::NKC, LA = 3;
+  u32x4 fr[LA + 1];
 #pragma unroll
-  for (int kb = 0; kb < S::NKB; ++kb)
+  for (int i = 0; i < LA; ++i) fr[i] = k_frag<D>(kst, la, i / S::NKC, i % S::NKC);
 #pragma unroll
-    for (int kc = 0; kc < S::NKC; ++kc)
-      s[kb] = mfma_qk<IS_BF16>(k_frag<D>(kst, la, kb, kc), qf[kc], kc == 0 ? f32x16{} : s[kb]);
+  for (int i = 0; i < NM; ++i) {
+    const int ia = i + LA;
+    if (ia < NM) fr[ia % (LA + 1)] = k_frag<D>(kst, la, ia / S::NKC, ia % S::NKC);
+    const int kb = i / S::NKC, kc = i % S::NKC;
+    s[kb] = mfma_qk<IS_BF16>(fr[i % (LA + 1)], qf[kc], kc == 0 ? f32x16{} : s[kb]);
+  }
 }
 
 // Per-lane online-softmax state: one query row, half of each tile's keys.
@@ -410,6 +428,8 @@ struct Pipe16 {
   __device__ __forceinline__ uint16_t *vstage(int par) const {
     return lds + (kKStages + par) * Shape16<D>::TILE_ELEMS;
   }
+  // The query tile (BLOCK_M rows, K's layout) after the rings.
+  __device__ __forceinline__ uint16_t *qstage() const { return lds + Shape16<D>::RING_ELEMS; }
   // Tile copies. Iteration j reads K_{j+1} and V_j. Its first steps issue
   // V_{j+1}, then K_{j+2}, into the stages V_{j-1} and K_j left (free since
   // the barrier that ended iteration j-1); a late step waits for V_{j+1}
@@ -424,6 +444,18 @@ struct Pipe16 {
   __device__ __forceinline__ void copy_v(u32x4 r, int t, int c) const {
     constexpr int TB = Shape16<D>::TILE_BYTES;
     dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * Shape16<D>::INS_BYTES, v_dma[c]);
+  }
+  // Copy of the workgroup's query tile (rows m0 ..; rows past N read as 0).
+  __device__ __forceinline__ void issue_q(const uint16_t *Qh, int m0) const {
+    using S = Shape16<D>;
+    const int rows = min(N - m0, S::BLOCK_M);
+    const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * D);
+    const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
+                     (uint32_t)__builtin_amdgcn_readfirstlane(rows * D * 2), (uint32_t)kBufferFlags};
+#pragma unroll
+    for (int c = 0; c < S::Q_INS; ++c)
+      dma16_to_lds(r, lds_wave + S::RING_ELEMS * 2 + c * S::INS_BYTES, k_dma[0] + c * S::INS_BYTES);
   }
   __device__ __forceinline__ void issue_k(int t) const {
     const u32x4 r = k_rsrc(t);
@@ -663,13 +695,13 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
 
 // Row-major staging of one wave's 32 x D block of O in LDS for the
 // epilogue: E bytes per element, rows of ROWB bytes (a whole row of O, or a
-// 256-byte part of it when longer: PASSES parts), CPR 16-byte chunks per row,
+// MAXROWB-byte part of it when longer: PASSES parts), CPR 16-byte chunks per row,
 // XOR-swizzled by row so the row-per-lane writes and the row-by-row reads
 // spread over the banks; one wave instruction reads RPI rows.
-template <int D, int E_>
+template <int D, int E_, int MAXROWB>
 struct OutStage {
   static constexpr int E = E_;
-  static constexpr int ROWB = D * E > 256 ? 256 : D * E;
+  static constexpr int ROWB = D * E > MAXROWB ? MAXROWB : D * E;
   static constexpr int PASSES = D * E / ROWB;
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPI = 64 / CPR;
@@ -682,8 +714,12 @@ struct OutStage {
 // already (fp16 inputs, or bf16 inputs whose V a first pass converted).
 // One query tile (BLOCK_M rows of head bh) from the load of Q to the stores
 // of O and LSE.
+// prefetched: the previous tile of this workgroup (same head) already copied
+// this tile's Q, V_0, K_0 and K_1. next_qt >= 0: copy that tile's ones once
+// this tile's loop is done.
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
-__device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int bh, int qt) {
+__device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int bh, int qt,
+                                          bool prefetched, int next_qt) {
   using S = Shape16<D>;
   constexpr int BN = S::BN;
   constexpr int NCB = S::NCB;
@@ -720,12 +756,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   // This lane's query row; rows past N use row N-1's data and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
   pp.qrow = r0 + l32;
-  const int qsrc = min(pp.qrow, N - 1);
 
-  u32x4 qf[NKC];
-#pragma unroll
-  for (int kc = 0; kc < NKC; ++kc)
-    qf[kc] = *reinterpret_cast<const u32x4 *>(Qh + (size_t)qsrc * D + kc * 16 + g * 8);
 
   // Key tiles to visit: for the workgroup (copies, barriers) and for this
   // wave (compute). Causal: only tiles holding some key <= the last row.
@@ -746,14 +777,24 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   st.neg_m = 0.f;
   st.l = 0.f;
 
-  // Prologue: V_0, K_0 and K_1 on their way; V_0 (converted) and S_0 once
-  // V_0 and K_0 are in; K_1 in before iteration 0.
-  pp.issue_v(0);
-  pp.issue_k(0);
-  pp.issue_k(1);
-  wait_vmcnt<S::DMA_INS>();  // V_0, K_0
+  // Prologue: the query tile, V_0, K_0 and K_1 on their way (the query
+  // tile through LDS: copied in whole rows, instead of 64 rows per load
+  // instruction); V_0 (converted), Q and S_0 once Q, V_0 and K_0 are in;
+  // K_1 in before iteration 0.
+  if (prefetched) {
+    wait_vmcnt<0>();  // also the previous tile's stores of O, issued later
+  } else {
+    pp.issue_q(Qh, m0);
+    pp.issue_v(0);
+    pp.issue_k(0);
+    pp.issue_k(1);
+    wait_vmcnt<S::DMA_INS>();  // Q, V_0, K_0
+  }
   pp.template convert_v<CONV_V>(0);
   lds_barrier();
+  u32x4 qf[NKC];  // Q[qrow][16kc + 8g .. +7], the B operand of QK^T
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) qf[kc] = k_frag<D>(pp.qstage(), pp.la, wave, kc);
   f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
   qk_tile<D, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
   if (nfw == 0)
@@ -768,6 +809,17 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   // Copies issued for tiles past the end (empty byte ranges) retire before
   // the workgroup's LDS can be handed to another one.
   wait_vmcnt<0>();
+  if (S::OWN_STAGE && next_qt >= 0) {
+    // Every wave has passed the loop's last barrier: no one reads the ring
+    // or the Q area any more. The next tile's first copies overlap this
+    // tile's epilogue.
+    const int m0n = next_qt * S::BLOCK_M;
+    pp.n_tiles = CAUSAL ? min(n_all, (m0n + S::BLOCK_M + BN - 1) / BN) : n_all;
+    pp.issue_q(Qh, m0n);
+    pp.issue_v(0);
+    pp.issue_k(0);
+    pp.issue_k(1);
+  }
 
   // Epilogue: combine the two key halves of the row sum, divide once, LSE.
   const float l_tot = sum_halves(st.l);
@@ -777,13 +829,15 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
     p.lse[(size_t)bh * N + pp.qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
   // O leaves through LDS. A lane holds one row, so stores straight from the
   // accumulators would touch 64 rows (64 cache lines) per instruction; staged
-  // row-major, each store instruction writes whole lines. Once every wave has
-  // passed this barrier none reads the K/V stages any more (and no copy is in
-  // flight), and each wave reuses its own slice of that memory.
-  lds_barrier();
-  using OS = OutStage<D, OUT_F32 ? 4 : 2>;
-  static_assert(S::WAVES * OS::WAVE_BYTES <= (kKStages + kVStages) * S::TILE_BYTES, "staging fits");
-  uint8_t *stage = reinterpret_cast<uint8_t *>(lds) + wave * OS::WAVE_BYTES;
+  // row-major, each store instruction writes whole lines. Each wave uses its
+  // own slice of the staging area; when that is the ring, it is free once
+  // every wave has passed this barrier (no copy is in flight).
+  if (!S::OWN_STAGE) lds_barrier();
+  using OS = OutStage<D, OUT_F32 ? 4 : 2, S::STAGE_ROWB>;
+  static_assert(S::WAVES * OS::WAVE_BYTES <= (S::OWN_STAGE ? S::STAGE_ELEMS * 2 : S::RING_ELEMS * 2),
+                "staging fits");
+  uint8_t *stage = reinterpret_cast<uint8_t *>(lds + (S::OWN_STAGE ? S::RING_ELEMS + S::BLOCK_M * D : 0)) +
+                   wave * OS::WAVE_BYTES;
   uint8_t *obase = static_cast<uint8_t *>(p.o) + (head + (size_t)r0 * D) * OS::E;
 #pragma unroll
   for (int ps = 0; ps < OS::PASSES; ++ps) {
@@ -832,12 +886,12 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
 __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[(kKStages + kVStages) * S::TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
   const int w = blockIdx.x;
   const int t = w / p.BH;
   const int bh = w - t * p.BH;
   if (!CAUSAL) {
-    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t);
+    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
     return;
   }
   const int qa = p.nq - 1 - t, qb = t;
@@ -846,7 +900,9 @@ __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void at
   for (int k = 0; k < n_items; ++k) {
     // The second tile's copies reuse the LDS the first one's epilogue read.
     if (k > 0) lds_barrier();
-    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb);
+    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb,
+                                                   S::OWN_STAGE && k > 0,
+                                                   k + 1 < n_items ? qb : -1);
   }
 }
 
