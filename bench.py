@@ -9,6 +9,12 @@ that is already resident in HBM. W untimed steps, then exactly K timed steps
 bracketed by torch.cuda.synchronize(); the kernel duration comes from HIP
 events recorded on the stream the kernel is launched on.
 
+The defaults (200 warm-up launches, 1000 timed) measure the sustained rate.
+The kernel draws the board's full power: coming out of idle, the first few
+launches run at a high clock, then the power controller pulls the clock down
+hard for some tens of launches before settling. Timing a few dozen launches
+right after a short warm-up lands in that dip and reads about 15% slow.
+
 Prints one JSON line. FLOPs count the two N x N x d contractions per head,
 halved when causal: 4*B*H*N^2*d (/2). Algorithmic bytes read Q, K, V once
 and write O and LSE once.
@@ -84,8 +90,8 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "in"])
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -881,15 +881,28 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 // and with one tile per workgroup the last workgroups to finish leave CUs
 // idle. A causal workgroup therefore takes tile nq-1-i and then tile i: all
 // pairs are equally long (the middle tile of an odd count runs alone, last).
-// Workgroup ids run pair-major, head-minor, so the 8 XCDs (round-robin over
-// ids) each keep the same heads.
+// Workgroups are handed to the 8 XCDs round-robin (id w runs on XCD w % 8)
+// and start in id order within an XCD. When B*H is a multiple of 8, the ids
+// of one XCD run head-major: all work items of head bh sit on XCD bh % 8 and
+// start together, so each head's K/V stream through that XCD's L2 about once
+// rather than once per wave of workgroups. Otherwise ids run item-major,
+// head-minor.
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
 __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
   using S = Shape16<D>;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
   const int w = blockIdx.x;
-  const int t = w / p.BH;
-  const int bh = w - t * p.BH;
+  int t, bh;
+  if ((p.BH & 7) == 0) {
+    const int per_head = CAUSAL ? (p.nq + 1) >> 1 : p.nq;
+    const int j = w >> 3;
+    const int hl = j / per_head;
+    t = j - hl * per_head;
+    bh = (hl << 3) | (w & 7);
+  } else {
+    t = w / p.BH;
+    bh = w - t * p.BH;
+  }
   if (!CAUSAL) {
     attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
     return;

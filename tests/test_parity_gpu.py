@@ -89,6 +89,11 @@ SMALL_CASES = [
     (1, 2, 257, 128, "bf16", False, 1.0),
     (1, 1, 511, 128, "f16", False, 1.0),
     (2, 1, 513, 128, "bf16", True, 2.0),
+    # B*H a multiple of 8: workgroup ids run head-major within each XCD
+    (2, 8, 700, 128, "bf16", True, 1.0),
+    (1, 16, 777, 128, "f16", False, 1.0),
+    (3, 8, 200, 64, "f16", False, 1.0),
+    (2, 12, 400, 64, "bf16", True, 1.0),
 ]
 
 
