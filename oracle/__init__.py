@@ -9,6 +9,9 @@ arithmetic.
 Contents
   attn_oracle(q, k, v, causal, scale, rows=None) -> (O, LSE)
       fp64 three-pass attention in C (``attn_oracle.c``), parallel over rows.
+  attn_bwd_oracle(q, k, v, dout, causal, scale, qrows=None, krows=None) -> (dQ, dK, dV)
+      fp64 attention gradients in C (``attn_bwd_oracle.c``), written out from
+      their definitions; dQ per query row, dK and dV per key row.
   attn_two_pass_np / attn_online_np
       tiny pure-NumPy fp64 variants used to pin the C oracle (brute force on
       small inputs); see ``variants.py``.
@@ -17,5 +20,6 @@ Parity status of each function is listed in ``variants.py`` and in the tests
 that pin them (``tests/test_oracle.py``).
 """
 from .native import (attn_oracle, oracle_threads, build_oracle, compile_oracle,  # noqa: F401
-                     open_oracle_library, library_path)
+                     open_oracle_library, library_path, attn_bwd_oracle,
+                     open_bwd_oracle_library, bwd_library_path)
 from .variants import attn_two_pass_np, attn_online_np  # noqa: F401

@@ -1,0 +1,216 @@
+/*
+ * Reference attention backward in fp64 -- TEST INFRASTRUCTURE ONLY.
+ *
+ * This file is the oracle that the GPU backward is checked against. Only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg may load it.
+ * It shares no code, header or constant with the HIP library (nor with the
+ * forward oracle) and is built by the host C compiler without fast-math.
+ *
+ * What it computes: the gradients of attention O = softmax(scale Q K^T [+
+ * causal mask]) V with respect to Q, K and V, given the upstream gradient dO,
+ * written out from the definitions that "4.4 Writing GPU Kernels with
+ * Triton", section "Kernel 5: FlashAttention Backward", recalls:
+ *
+ *   P_ij  = exp(s_ij - m_i) / l_i            (the softmax of row i; s_ij =
+ *                                             scale q_i . k_j over the visible
+ *                                             keys j, m_i their maximum,
+ *                                             l_i = sum_j exp(s_ij - m_i))
+ *   O_i   = sum_j P_ij v_j
+ *   dV_j  = sum_i P_ij dO_i                  (dV = P^T dO)
+ *   dP_ij = dO_i . v_j                       (dP = dO V^T)
+ *   D_i   = dO_i . O_i                       (rowsum(dO * O), the page's
+ *                                             "Preprocessing" section)
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dQ_i  = scale sum_j dS_ij k_j            (dQ = dS K, scaled)
+ *   dK_j  = scale sum_i dS_ij q_i            (dK = dS^T Q, scaled)
+ *
+ * The page writes the scale as 1/sqrt(d), its default; here it is the scale
+ * the forward used. With a causal mask, query i sees the keys j <= i; hidden
+ * pairs are left out of every sum (the same as P_ij = 0).
+ *
+ * dQ_i needs only row i. dK_j and dV_j need every row that sees key j, so
+ * for them the row statistics m_i, l_i and D_i of the whole head are found
+ * first (three passes per row, as in the forward's stable softmax).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARG 1
+#define ORACLE_NO_MEMORY 2
+
+static double dot(const double *a, const double *b, int64_t d) {
+  double s = 0.0;
+  for (int64_t c = 0; c < d; ++c) s += a[c] * b[c];
+  return s;
+}
+
+/* Row statistics of query i of one head: m_i, l_i, and D_i = dO_i . O_i with
+ * O_i formed here. `s` and `o_row` are scratch (N and d doubles). */
+static void row_stats(const double *q, const double *k, const double *v, const double *dout,
+                      int64_t N, int64_t d, int causal, double scale, int64_t i, double *s,
+                      double *o_row, double *m_out, double *l_out, double *D_out) {
+  const int64_t n_keys = causal ? i + 1 : N;
+  double m = -INFINITY;
+  for (int64_t j = 0; j < n_keys; ++j) {
+    s[j] = scale * dot(q + i * d, k + j * d, d);
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int64_t j = 0; j < n_keys; ++j) l += exp(s[j] - m);
+  for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
+  for (int64_t j = 0; j < n_keys; ++j) {
+    const double p = exp(s[j] - m) / l;
+    for (int64_t c = 0; c < d; ++c) o_row[c] += p * v[j * d + c];
+  }
+  *m_out = m;
+  *l_out = l;
+  *D_out = dot(dout + i * d, o_row, d);
+}
+
+/* dQ_i of one head. */
+static void dq_row(const double *q, const double *k, const double *v, const double *dout,
+                   int64_t N, int64_t d, int causal, double scale, int64_t i, double *s,
+                   double *o_row, double *dq) {
+  double m, l, D;
+  row_stats(q, k, v, dout, N, d, causal, scale, i, s, o_row, &m, &l, &D);
+  const int64_t n_keys = causal ? i + 1 : N;
+  for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;
+  for (int64_t j = 0; j < n_keys; ++j) {
+    const double p = exp(scale * dot(q + i * d, k + j * d, d) - m) / l;
+    const double dp = dot(dout + i * d, v + j * d, d);
+    const double ds = p * (dp - D);
+    for (int64_t c = 0; c < d; ++c) dq[c] += ds * k[j * d + c];
+  }
+  for (int64_t c = 0; c < d; ++c) dq[c] *= scale;
+}
+
+/* dK_j and dV_j of one head from the head's row statistics. */
+static void dkdv_row(const double *q, const double *k, const double *v, const double *dout,
+                     int64_t N, int64_t d, int causal, double scale, int64_t j,
+                     const double *m, const double *l, const double *D, double *dk,
+                     double *dv) {
+  for (int64_t c = 0; c < d; ++c) dk[c] = dv[c] = 0.0;
+  const int64_t i0 = causal ? j : 0; /* the rows that see key j */
+  for (int64_t i = i0; i < N; ++i) {
+    const double p = exp(scale * dot(q + i * d, k + j * d, d) - m[i]) / l[i];
+    const double dp = dot(dout + i * d, v + j * d, d);
+    const double ds = p * (dp - D[i]);
+    for (int64_t c = 0; c < d; ++c) {
+      dv[c] += p * dout[i * d + c];
+      dk[c] += ds * q[i * d + c];
+    }
+  }
+  for (int64_t c = 0; c < d; ++c) dk[c] *= scale;
+}
+
+/*
+ * attn_bwd_oracle_rows -- gradients for lists of query and key rows.
+ *
+ * q, k, v, dout : [B][H][N][d] row-major fp64 (callers upcast the exact
+ *                 values the GPU receives).
+ * qrows / nq    : flat query row ids (b*H + h)*N + i whose dQ is wanted, or
+ *                 NULL with nq = B*H*N for all of them in order.
+ * krows / nk    : flat key row ids whose dK and dV are wanted, or NULL with
+ *                 nk = B*H*N for all.
+ * dq            : [nq][d] out;  dk, dv : [nk][d] out.
+ * nthreads      : OpenMP threads (<= 0: the runtime default).
+ * Returns ORACLE_OK, ORACLE_BAD_ARG or ORACLE_NO_MEMORY.
+ */
+int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, const double *dout,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, double scale,
+                         const int64_t *qrows, int64_t nq, double *dq, const int64_t *krows,
+                         int64_t nk, double *dk, double *dv, int nthreads) {
+  if (!q || !k || !v || !dout) return ORACLE_BAD_ARG;
+  if (B < 1 || H < 1 || N < 1 || d < 1 || nq < 0 || nk < 0) return ORACLE_BAD_ARG;
+  if ((nq > 0 && !dq) || (nk > 0 && (!dk || !dv))) return ORACLE_BAD_ARG;
+  const int64_t BH = B * H, total = BH * N;
+  if ((!qrows && nq != 0 && nq != total) || (!krows && nk != 0 && nk != total))
+    return ORACLE_BAD_ARG;
+  for (int64_t r = 0; qrows && r < nq; ++r)
+    if (qrows[r] < 0 || qrows[r] >= total) return ORACLE_BAD_ARG;
+  for (int64_t r = 0; krows && r < nk; ++r)
+    if (krows[r] < 0 || krows[r] >= total) return ORACLE_BAD_ARG;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#endif
+  int bad = 0;
+
+  /* dQ: independent rows. */
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+  {
+    double *s = (double *)malloc((size_t)(N + d) * sizeof(double));
+    if (!s) {
+      bad = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 8)
+#endif
+      for (int64_t r = 0; r < nq; ++r) {
+        const int64_t flat = qrows ? qrows[r] : r;
+        const int64_t bh = flat / N, i = flat % N;
+        const size_t head = (size_t)bh * (size_t)N * (size_t)d;
+        dq_row(q + head, k + head, v + head, dout + head, N, d, causal, scale, i, s, s + N,
+               dq + r * d);
+      }
+      free(s);
+    }
+  }
+  if (bad) return ORACLE_NO_MEMORY;
+  if (nk == 0) return ORACLE_OK;
+
+  /* dK, dV: row statistics of every head that a requested key belongs to. */
+  char *need = (char *)calloc((size_t)BH, 1);
+  double *m = (double *)malloc((size_t)total * sizeof(double));
+  double *l = (double *)malloc((size_t)total * sizeof(double));
+  double *D = (double *)malloc((size_t)total * sizeof(double));
+  if (!need || !m || !l || !D) {
+    free(need), free(m), free(l), free(D);
+    return ORACLE_NO_MEMORY;
+  }
+  for (int64_t r = 0; r < nk; ++r) need[(krows ? krows[r] : r) / N] = 1;
+#ifdef _OPENMP
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+#endif
+  {
+    double *s = (double *)malloc((size_t)(N + d) * sizeof(double));
+    if (!s) {
+      bad = 1;
+    } else {
+#ifdef _OPENMP
+#pragma omp for schedule(dynamic, 8)
+#endif
+      for (int64_t flat = 0; flat < total; ++flat) {
+        const int64_t bh = flat / N, i = flat % N;
+        if (!need[bh]) continue;
+        const size_t head = (size_t)bh * (size_t)N * (size_t)d;
+        row_stats(q + head, k + head, v + head, dout + head, N, d, causal, scale, i, s, s + N,
+                  m + flat, l + flat, D + flat);
+      }
+      free(s);
+    }
+  }
+  if (!bad) {
+#ifdef _OPENMP
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 8)
+#endif
+    for (int64_t r = 0; r < nk; ++r) {
+      const int64_t flat = krows ? krows[r] : r;
+      const int64_t bh = flat / N, j = flat % N;
+      const size_t head = (size_t)bh * (size_t)N * (size_t)d;
+      const size_t rows = (size_t)bh * (size_t)N;
+      dkdv_row(q + head, k + head, v + head, dout + head, N, d, causal, scale, j, m + rows,
+               l + rows, D + rows, dk + r * d, dv + r * d);
+    }
+  }
+  free(need), free(m), free(l), free(D);
+  (void)nthreads;
+  return bad ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
