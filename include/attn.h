@@ -1,7 +1,7 @@
 /*
- * attn.h -- C ABI of the gfx950 (MI355X) attention forward library
- * (libattn_fwd.so). Plain C: no C++ types, no exceptions across the
- * boundary, no torch types. Device pointers are HIP device pointers; the
+ * attn.h -- C ABI of the gfx950 (MI355X) attention library (libattn_fwd.so):
+ * the FlashAttention forward and backward. Plain C: no C++ types, no
+ * exceptions across the boundary, no torch types. Device pointers are HIP device pointers; the
  * stream is a hipStream_t passed as void* (NULL = the default stream).
  *
  * Operation (the FlashAttention forward of "4.4 Writing GPU Kernels with
@@ -43,7 +43,8 @@ typedef enum {
   ATTN_ERR_SHAPE = 2,        /* B, H or N < 1, or a size beyond the limits below */
   ATTN_ERR_UNSUPPORTED = 3,  /* head dim or dtype combination not built */
   ATTN_ERR_SCALE = 4,        /* scale is NaN, infinite or negative */
-  ATTN_ERR_HIP = 5           /* the HIP runtime reported an error at launch */
+  ATTN_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
+  ATTN_ERR_WORKSPACE = 6     /* a required workspace is NULL, too small or misaligned */
 } attn_status;
 
 /* Version of this ABI (bumped on any incompatible change). */
@@ -119,6 +120,61 @@ attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, fl
                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
                         attn_dtype in_dtype, attn_dtype out_dtype, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs:
+ * 8 bytes per query row (B*H*N rows), rounded up to 256; 0 for an invalid
+ * problem (sizes out of range or d not 64 or 128). No HIP call is made.
+ */
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * attn_bwd -- enqueue the attention backward on `stream`.
+ *
+ * Operation (the FlashAttention backward of "4.4 Writing GPU Kernels with
+ * Triton", section "Kernel 5: FlashAttention Backward", including its
+ * preprocessing step): given the forward's inputs, its output O, its
+ * natural-log LSE and the upstream gradient dO, for every batch b and head h
+ *
+ *   P_ij  = exp(s_ij - LSE_i)      (s_ij as in attn_fwd; 0 for hidden keys)
+ *   D_i   = sum_c dO_ic O_ic
+ *   dS_ij = P_ij (sum_c dO_ic V_jc - D_i)
+ *   dQ_i  = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
+ *   dV_j  = sum_i P_ij dO_i.
+ *
+ * P is rebuilt tile by tile from LSE; no N x N tensor is written. A first
+ * pass writes (LSE * log2 e, D) per row into the workspace; a key-parallel
+ * kernel then writes dK and dV, and a query-parallel kernel writes dQ (no
+ * atomics: the result is deterministic).
+ *
+ * q, k, v, dout : device, [B][H][N][d] contiguous, element type in_dtype
+ *                 (BF16 or F16).
+ * o             : device, [B][H][N][d] contiguous, element type o_dtype
+ *                 (in_dtype or F32): the forward's output.
+ * lse           : device, [B][H][N] contiguous fp32: the forward's LSE.
+ * dq, dk, dv    : device, [B][H][N][d] contiguous, element type grad_dtype
+ *                 (in_dtype or F32); written.
+ * B, H, N, d, causal, scale : as for attn_fwd (the forward's values).
+ * workspace     : device, at least attn_bwd_workspace_bytes() bytes, 16-byte
+ *                 aligned; caller-owned, contents on entry irrelevant and
+ *                 unspecified afterwards. It must not be used by other work
+ *                 until this call's work on `stream` has finished.
+ * stream        : hipStream_t (or NULL); the call only enqueues work.
+ *
+ * Precision: Q K^T, dO V^T and the three gradient products run on the
+ * matrix cores in the input type with fp32 accumulation; P and dS are
+ * rounded to the input type for the products that take them, and every
+ * other quantity is fp32. fp32 inputs are not supported by the backward
+ * (ATTN_ERR_UNSUPPORTED).
+ * Limits and errors: those of attn_fwd, plus ATTN_ERR_WORKSPACE when the
+ * workspace is NULL, too small or misaligned. Every argument is validated
+ * before any HIP call. Outputs must not alias inputs (not checked).
+ */
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
+                     attn_dtype o_dtype, attn_dtype grad_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(attn_status s);

@@ -1,7 +1,7 @@
 """Thin ctypes binding of libattn_fwd.so (the C ABI in include/attn.h).
 
-Argument marshalling only: every step of the attention forward runs in the
-library's HIP kernels. torch supplies the device buffers and the stream.
+Argument marshalling only: every step of the attention forward and backward
+runs in the library's HIP kernels. torch supplies the device buffers and the stream.
 There is no fallback: if the library cannot be loaded the call raises.
 """
 import ctypes
@@ -15,9 +15,10 @@ LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 # attn_dtype / attn_status values of include/attn.h
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
-          4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP"}
-EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_status_string",
-           "attn_abi_version", "attn_last_hip_error")
+          4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE"}
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_bwd",
+           "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version",
+           "attn_last_hip_error")
 
 _TORCH_TO_ATTN = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
 _lib = None
@@ -47,6 +48,12 @@ def load_library(path=LIB_PATH):
                                 ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
+                             ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                             ctypes.c_size_t, vp]
+    lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
     lib.attn_abi_version.restype = ctypes.c_int
@@ -143,3 +150,63 @@ def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=No
             msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
         raise AttnError(st, msg)
     return out, lse
+
+
+def attn_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, N, d,
+                 causal, scale, in_dtype, o_dtype, grad_dtype, ws_ptr, ws_bytes, stream=None):
+    """Direct call of attn_bwd with integer pointers; returns the status."""
+    return load_library().attn_bwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                   dv_ptr, int(B), int(H), int(N), int(d), int(bool(causal)),
+                                   float(scale), int(in_dtype), int(o_dtype), int(grad_dtype),
+                                   ws_ptr, int(ws_bytes), stream)
+
+
+def bwd_workspace_bytes(B, H, N, d):
+    """Bytes of device workspace attn_bwd needs (0 for an invalid problem)."""
+    return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, workspace=None):
+    """Attention backward on the current HIP stream: (dq, dk, dv) for the
+    upstream gradient dout, given the forward's inputs, its output o (input
+    dtype or float32) and its lse. grad_dtype defaults to the input dtype
+    (torch.float32 is also accepted). The workspace (a uint8 tensor of at
+    least bwd_workspace_bytes(...) bytes) is taken from torch's allocator when
+    not given.
+    """
+    if q.dim() != 4 or any(x.shape != q.shape for x in (k, v, o, dout)):
+        raise ValueError("q, k, v, o, dout must all be [B, H, N, d] of one shape")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in (torch.float16,
+                                                                            torch.bfloat16):
+        raise ValueError("q, k, v, dout must share one dtype, float16 or bfloat16")
+    tensors = (q, k, v, o, lse, dout)
+    if not (q.is_cuda and all(x.device == q.device for x in tensors)):
+        raise ValueError("all tensors must be on one GPU")
+    if not all(x.is_contiguous() for x in tensors):
+        raise ValueError("all tensors must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be a [B, H, N] float32 tensor")
+    if o.dtype not in (q.dtype, torch.float32):
+        raise ValueError("o must be in the input dtype or float32")
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    grad_dtype = grad_dtype or q.dtype
+    if grad_dtype not in (q.dtype, torch.float32):
+        raise ValueError("grad_dtype must be the input dtype or float32")
+    dq, dk, dv = (torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3))
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                      causal, scale, _TORCH_TO_ATTN[q.dtype], _TORCH_TO_ATTN[o.dtype],
+                      _TORCH_TO_ATTN[grad_dtype], workspace.data_ptr(),
+                      workspace.numel() * workspace.element_size(), stream)
+    if st != 0:
+        msg = status_string(st)
+        if st == 5:
+            msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
+        raise AttnError(st, msg)
+    return dq, dk, dv

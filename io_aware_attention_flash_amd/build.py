@@ -1,5 +1,8 @@
 """Build libattn_fwd.so (the gfx950 HIP kernels and the C ABI) in-tree.
 
+The library holds the forward (csrc/attn_fwd.hip) and the backward
+(csrc/attn_bwd.hip).
+
     python -m io_aware_attention_flash_amd.build
 
 hipcc cross-compiles for gfx950 on a machine without a GPU. Packed-fp32
@@ -15,7 +18,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "attn_fwd.hip")
+SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")
@@ -46,7 +49,7 @@ def scratch_users(remarks):
 def build(verbose=False, extra=()):
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + ["-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc] + HIPCC_FLAGS + list(extra) + ["-I", INCLUDE] + SRCS + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -66,7 +69,7 @@ def is_stale():
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    srcs = [SRC, os.path.join(INCLUDE, "attn.h")]
+    srcs = SRCS + [os.path.join(INCLUDE, "attn.h")]
     return any(os.path.getmtime(s) > t for s in srcs)
 
 

@@ -1,0 +1,691 @@
+// FlashAttention backward for gfx950 (MI355X): dQ, dK, dV of
+// O = softmax(scale Q K^T [+ causal mask]) V from the upstream gradient dO,
+// the forward's O and its per-row natural-log logsumexp L.
+//
+// The method is that of "4.4 Writing GPU Kernels with Triton", section
+// "Kernel 5: FlashAttention Backward": the softmax weights are rebuilt tile by
+// tile from L (P = exp(S - L), no N x N tensor in memory), D_i = rowsum(dO_i *
+// O_i) collapses the softmax Jacobian, dS = P * (dP - D), dV = P^T dO,
+// dK = scale dS^T Q and dQ = scale dS K. The page's closing notes describe
+// the atomic-free split used here: a key-parallel kernel owns dK and dV, a
+// query-parallel kernel owns dQ, and neither writes the other's rows, so
+// there are no atomics and the result is deterministic.
+//
+// Three launches on the caller's stream:
+//   bwd_prep : LD[row] = (L * log2(e), D) per query row, into the workspace.
+//   bwd_dkdv : one workgroup per (head, 128 keys); 4 waves of 32 keys each
+//              loop over 32-query tiles. Per tile and wave, on the matrix
+//              cores (v_mfma_f32_32x32x16, fp32 accumulate):
+//                S = Q K^T, P = exp2(S*qk - L*log2 e), dV^T += dO^T P,
+//                dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS.
+//              K stays in registers, V in LDS; Q, dO and LD tiles stream
+//              through a two-stage LDS ring filled by buffer_load ... lds.
+//   bwd_dq   : one workgroup per (head, 128 queries); 4 waves of 32 queries
+//              loop over 64-key tiles: S^T = K Q^T, P, dP^T = V dO^T,
+//              dS, dQ^T += K^T dS^T. Q and dO stay in registers; K and V
+//              tiles stream through a two-stage LDS ring.
+// P and dS enter the matrix cores in the input type (bf16 or fp16), as the
+// page casts them to the operand type; S, P, dP, dS and every accumulator
+// are fp32.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn_internal {
+void set_last_hip_error(int e);
+}
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;  // 4 waves
+constexpr int kBlockK = 128;   // keys per dK/dV workgroup (32 per wave)
+constexpr int kTileQ = 32;     // queries per dK/dV step
+constexpr int kBlockQ = 128;   // queries per dQ workgroup (32 per wave)
+constexpr int kTileK = 64;     // keys per dQ step
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct BwdParams {
+  const void *q, *k, *v, *o, *dout;
+  const float *lse;
+  void *dq, *dk, *dv;
+  f32x2 *ld;  // workspace: (L * log2 e, D) per query row
+  int N;
+  int BH;
+  float qk;     // scale * log2(e)
+  float scale;  // applied to dQ and dK
+};
+
+// ---------------------------------------------------------------------------
+// LDS tiles: rows of D 16-bit elements, 16-byte chunks XOR-swizzled by row so
+// that both reads below are free of bank conflicts:
+//  - row reads (a lane takes 16 bytes of one row; 16 lanes read 16 rows);
+//  - transposing reads (ds_read_b64_tr_b16: 16 lanes read 4 rows x 4
+//    columns of 4 elements).
+// The swizzle depends on the row modulo 16 only.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  const int r = (row >> 1) & 7;
+  return ((r & 3) << 1) | (r >> 2);
+}
+
+// 16 bytes of row `row`, logical chunk `chunk` (elements 8*chunk .. +7).
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const uint16_t *tile, int row, int chunk) {
+  return *reinterpret_cast<const u32x4 *>(tile + row * D + ((chunk ^ swz<D>(row)) << 3));
+}
+
+// Lane-constant offsets of the transposing reads: for column block cb and
+// half u, the element offset (relative to row 16t) of the 4-element piece
+// this lane supplies. In a 16-lane block (g, h) lane s = a + 4m supplies row
+// 8u + 4g + m, columns 32cb + 16h + 4a .. +3.
+template <int D>
+struct TrAddr {
+  int off[D / 32][2];
+};
+
+template <int D>
+__device__ __forceinline__ TrAddr<D> tr_addr(int lane) {
+  TrAddr<D> ta;
+  const int g = lane >> 5, h = (lane >> 4) & 1, s = lane & 15;
+  const int a = s & 3, m = s >> 2;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * u + 4 * g + m;
+#pragma unroll
+    for (int cb = 0; cb < D / 32; ++cb) {
+      const int x = 4 * cb + 2 * h + (a >> 1);
+      ta.off[cb][u] = row * D + ((x ^ swz<D>(row)) << 3) + (a & 1) * 4;
+    }
+  }
+  return ta;
+}
+
+// Operand of one 32x32x16 step contracting over 16 rows 16t .. 16t+15 of a
+// row-major tile: lane l gets column 32cb + (l & 31) at rows
+// 16t + 4g + 0..3 (k slots 8g + 0..3) and 16t + 8 + 4g + 0..3 (8g + 4..7),
+// g = l >> 5 -- the row order of the 32x32 accumulator layout, so the other
+// operand can come straight from an accumulator (acc_frag below).
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const TrAddr<D> &ta, int t, int cb) {
+  const uint16_t *p = tile + 16 * t * D;
+  const s16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p + ta.off[cb][0]));
+  const s16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4 *)(p + ta.off[cb][1]));
+  const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
+  return u32x4{w0[0], w0[1], w1[0], w1[1]};
+}
+
+// fp32 pair -> packed bf16 / fp16, round to nearest even.
+template <bool IS_BF16>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (IS_BF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  } else {
+    f16x2 h = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
+  }
+}
+
+// Elements 8t .. 8t+7 of a 32x32 accumulator (rows 16t + 4g + 0..3 and
+// 16t + 8 + 4g + 0..3 of the lane's column) as one 16-step operand.
+template <bool IS_BF16>
+__device__ __forceinline__ u32x4 acc_frag(const f32x16 &x, int t) {
+  return u32x4{pack2<IS_BF16>(x[8 * t + 0], x[8 * t + 1]), pack2<IS_BF16>(x[8 * t + 2], x[8 * t + 3]),
+               pack2<IS_BF16>(x[8 * t + 4], x[8 * t + 5]), pack2<IS_BF16>(x[8 * t + 6], x[8 * t + 7])};
+}
+
+template <bool IS_BF16>
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (IS_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Copies into LDS: buffer_load_dwordx4 ... lds moves 16 bytes per lane from
+// the descriptor's range (reads past it return zeros) to LDS at M0 + 16*lane.
+// Written as inline assembly so the compiler does not treat the copies in
+// flight as writers of every LDS location; the kernels order them with an
+// explicit vmcnt wait and a barrier.
+// ---------------------------------------------------------------------------
+constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer descriptor
+
+__device__ __forceinline__ u32x4 make_rsrc(const void *base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kBufferFlags};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+__device__ __forceinline__ void dma16(u32x4 rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+// Tile of R rows x D 16-bit elements, copied by all 256 threads: instruction
+// c fills 16-byte slots c*256 + tid; slot s holds physical chunk s % CPR of
+// row s / CPR, i.e. logical chunk (s % CPR) ^ swz(row). One instruction spans
+// a whole number of swizzle periods (16 rows), so the lane's source offset
+// is that of c = 0 plus c * 4096 bytes.
+template <int D, int R>
+struct TileCopy {
+  static constexpr int CPR = D / 8;
+  static constexpr int INS = R * CPR / kThreads;
+  static_assert(INS * kThreads == R * CPR && (kThreads / CPR) % 16 == 0, "tile copy shape");
+  __device__ static uint32_t src_offset(int tid) {
+    const int row = tid / CPR;
+    return row * D * 2 + (((tid % CPR) ^ swz<D>(row)) << 4);
+  }
+  // rows [r0, r0 + R) of a head of N rows into the tile at `lds`.
+  __device__ static void issue(const uint16_t *head, int r0, int N, uint16_t *lds, uint32_t voff,
+                               int wave) {
+    const int rows = min(N - r0, R);
+    const u32x4 rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)(rows > 0 ? rows : 0) * D * 2);
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 64 * 16);
+#pragma unroll
+    for (int c = 0; c < INS; ++c) dma16(rs, base + c * kThreads * 16, voff + c * kThreads * 16);
+  }
+};
+
+// Halves of a packed fp16 pair as fp32 (exact).
+__device__ __forceinline__ float f16_lo_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep: LD[r] = (L_r * log2 e, D_r = sum_c dO[r,c] O[r,c]) for every
+// query row r (B*H*N rows). 16 lanes per row, 8 columns each (d = 128), or
+// 8 lanes per row (d = 64).
+// ---------------------------------------------------------------------------
+template <int D, bool IS_BF16, bool O_F32>
+__global__ __launch_bounds__(256) void bwd_prep(BwdParams p, int64_t rows) {
+  constexpr int LPR = D / 8;  // lanes per row
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t r = gid / LPR;
+  const int part = (int)(gid % LPR);
+  float acc = 0.f;
+  if (r < rows) {
+    const size_t e0 = (size_t)r * D + part * 8;
+    const u32x4 dw = *reinterpret_cast<const u32x4 *>(
+        reinterpret_cast<const uint16_t *>(p.dout) + e0);
+    float dof[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (IS_BF16) {
+        dof[2 * i] = __uint_as_float(dw[i] << 16);
+        dof[2 * i + 1] = __uint_as_float(dw[i] & 0xffff0000u);
+      } else {
+        dof[2 * i] = f16_lo_to_f32(dw[i]);
+        dof[2 * i + 1] = f16_hi_to_f32(dw[i]);
+      }
+    }
+    if constexpr (O_F32) {
+      const f32x4 o0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.o) + e0);
+      const f32x4 o1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.o) + e0 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc += dof[i] * o0[i] + dof[4 + i] * o1[i];
+    } else {
+      const u32x4 ow = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(p.o) + e0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float lo, hi;
+        if constexpr (IS_BF16) {
+          lo = __uint_as_float(ow[i] << 16);
+          hi = __uint_as_float(ow[i] & 0xffff0000u);
+        } else {
+          lo = f16_lo_to_f32(ow[i]);
+          hi = f16_hi_to_f32(ow[i]);
+        }
+        acc += dof[2 * i] * lo + dof[2 * i + 1] * hi;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (r < rows && part == 0) p.ld[r] = f32x2{p.lse[r] * kLog2e, acc};
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dkdv
+// ---------------------------------------------------------------------------
+template <int D>
+struct DkdvShape {
+  static constexpr int TILE = kTileQ * D;           // elements of a Q or dO tile
+  static constexpr int STAGE = 2 * TILE + 512;      // Q, dO, LD (1 KB: one copy instruction)
+  static constexpr int V_ELEMS = kBlockK * D;
+  static constexpr int LDS_ELEMS = V_ELEMS + 2 * STAGE;
+};
+
+template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
+  using S = DkdvShape<D>;
+  using QCopy = TileCopy<D, kTileQ>;
+  using VCopy = TileCopy<D, kBlockK>;
+  constexpr int NKC = D / 16, NCB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int kbk = blockIdx.x / p.BH;  // small k0 first: causal blocks with most work start first
+  const int bh = blockIdx.x - kbk * p.BH;
+  const int N = p.N;
+  const int k0 = kbk * kBlockK, kw0 = k0 + 32 * wave;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head;
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head;
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head;
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head;
+  const f32x2 *LDh = p.ld + (size_t)bh * N;
+
+  uint16_t *vlds = lds;
+  auto stage = [&](int s) { return lds + S::V_ELEMS + s * S::STAGE; };
+
+  const uint32_t qvoff = QCopy::src_offset(tid);
+  const int q_begin = CAUSAL ? k0 : 0;
+  const int n_qt = (N - q_begin + kTileQ - 1) / kTileQ;
+
+  // Copies of query tile `it` into stage it & 1: Q and dO by every wave, LD by wave 0.
+  auto issue = [&](int it) {
+    const int q0 = q_begin + it * kTileQ;
+    uint16_t *st = stage(it & 1);
+    QCopy::issue(Qh, q0, N, st, qvoff, wave);
+    QCopy::issue(dOh, q0, N, st + S::TILE, qvoff, wave);
+    if (wave == 0) {
+      const int rows = min(N - q0, kTileQ);
+      const u32x4 rs = make_rsrc(LDh + q0, (uint32_t)rows * 8);
+      dma16(rs, __builtin_amdgcn_readfirstlane(lds_addr(st + 2 * S::TILE)), lane * 16);
+    }
+  };
+
+  // V block (this workgroup's 128 keys) into LDS, and the first query tile.
+  VCopy::issue(Vh, k0, N, vlds, VCopy::src_offset(tid), wave);
+  issue(0);
+
+  // K operand of S = Q K^T for this wave's keys: K[kw0 + l32][16kc + 8g ..].
+  u32x4 kf[NKC];
+  {
+    const bool ok = kw0 + l32 < N;
+    const uint16_t *kr = Kh + (size_t)(ok ? kw0 + l32 : 0) * D + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      kf[kc] = ok ? *reinterpret_cast<const u32x4 *>(kr + 16 * kc) : u32x4{0, 0, 0, 0};
+  }
+  const TrAddr<D> ta = tr_addr<D>(lane);
+  f32x16 dvt[NCB], dkt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dvt[cb] = dkt[cb] = f32x16{};
+  const int my_key = kw0 + l32;
+  const float qk = p.qk;
+
+#pragma unroll 1
+  for (int it = 0; it < n_qt; ++it) {
+    const int q0 = q_begin + it * kTileQ;
+    if (it + 1 < n_qt) {
+      issue(it + 1);
+      if (wave == 0) wait_vmcnt<2 * QCopy::INS + 1>(); else wait_vmcnt<2 * QCopy::INS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const uint16_t *qt = stage(it & 1), *dot = qt + S::TILE;
+    const f32x4 *ldt = reinterpret_cast<const f32x4 *>(qt + 2 * S::TILE);  // (L2, D) pairs
+    // Whole tile above this wave's keys (causal): nothing to add.
+    if (!CAUSAL || q0 + kTileQ - 1 >= kw0) {
+      // S = Q K^T and dP = dO V^T: lane (key my_key) holds queries
+      // q0 + 8j + 4g + r in element 4j + r of each.
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) {
+        s = mfma<IS_BF16>(row_frag<D>(qt, l32, 2 * kc + g), kf[kc], s);
+        dp = mfma<IS_BF16>(row_frag<D>(dot, l32, 2 * kc + g),
+                           row_frag<D>(vlds, 32 * wave + l32, 2 * kc + g), dp);
+      }
+      // P = exp2(S * qk - L2), with masked pairs (key after query, key or
+      // query past the end) set to 0; dS = P (dP - D). Both packed as the
+      // operands of the two accumulating products.
+      const bool edge = (CAUSAL && q0 < kw0 + 32) || kw0 + 32 > N || q0 + kTileQ > N;
+      uint32_t pp[8], dsp[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 a = ldt[4 * j + 2 * g], b = ldt[4 * j + 2 * g + 1];  // rows 8j+4g .. +3
+        const float l2[4] = {a[0], a[2], b[0], b[2]};
+        const float dd[4] = {a[1], a[3], b[1], b[3]};
+        float pr[4], dr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float x = __builtin_amdgcn_exp2f(s[4 * j + r] * qk - l2[r]);
+          if (edge) {
+            const int qrow = q0 + 8 * j + 4 * g + r;
+            const bool keep = (!CAUSAL || my_key <= qrow) && my_key < N && qrow < N;
+            x = keep ? x : 0.f;
+          }
+          pr[r] = x;
+          dr[r] = x * (dp[4 * j + r] - dd[r]);
+        }
+        pp[2 * j] = pack2<IS_BF16>(pr[0], pr[1]);
+        pp[2 * j + 1] = pack2<IS_BF16>(pr[2], pr[3]);
+        dsp[2 * j] = pack2<IS_BF16>(dr[0], dr[1]);
+        dsp[2 * j + 1] = pack2<IS_BF16>(dr[2], dr[3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (operand t: elements 8t .. 8t+7)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
+        const u32x4 df = {dsp[4 * t], dsp[4 * t + 1], dsp[4 * t + 2], dsp[4 * t + 3]};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          dvt[cb] = mfma<IS_BF16>(tr_frag<D>(dot, ta, t, cb), pf, dvt[cb]);
+          dkt[cb] = mfma<IS_BF16>(tr_frag<D>(qt, ta, t, cb), df, dkt[cb]);
+        }
+      }
+    }
+    lds_barrier();  // stage it & 1 is refilled by the next iteration's copies
+  }
+
+  // dV^T / dK^T accumulators: lane holds key my_key, columns 32cb + 8j + 4g + 0..3.
+  if (my_key < N) {
+    const size_t row = (size_t)bh * N + my_key;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * cb + 8 * j + 4 * g;
+        const f32x4 v4 = {dvt[cb][4 * j], dvt[cb][4 * j + 1], dvt[cb][4 * j + 2], dvt[cb][4 * j + 3]};
+        const f32x4 k4 = {dkt[cb][4 * j] * p.scale, dkt[cb][4 * j + 1] * p.scale,
+                          dkt[cb][4 * j + 2] * p.scale, dkt[cb][4 * j + 3] * p.scale};
+        if constexpr (GRAD_F32) {
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dv) + row * D + c) = v4;
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dk) + row * D + c) = k4;
+        } else {
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dv) + row * D + c) =
+              u32x2{pack2<IS_BF16>(v4[0], v4[1]), pack2<IS_BF16>(v4[2], v4[3])};
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dk) + row * D + c) =
+              u32x2{pack2<IS_BF16>(k4[0], k4[1]), pack2<IS_BF16>(k4[2], k4[3])};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_dq
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqShape {
+  static constexpr int TILE = kTileK * D;  // elements of a K or V tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LDS_ELEMS = 2 * STAGE;
+};
+
+template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
+  using S = DqShape<D>;
+  using KCopy = TileCopy<D, kTileK>;
+  constexpr int NKC = D / 16, NCB = D / 32;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int N = p.N;
+  const int nqb = (N + kBlockQ - 1) / kBlockQ;
+  const int t_ = blockIdx.x / p.BH;
+  const int bh = blockIdx.x - t_ * p.BH;
+  const int qb = CAUSAL ? nqb - 1 - t_ : t_;  // causal: longest first
+  const int m0 = qb * kBlockQ, qw0 = m0 + 32 * wave;
+  const int my_q = qw0 + l32;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head;
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head;
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head;
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head;
+
+  const uint32_t kvoff = KCopy::src_offset(tid);
+  const int kend = CAUSAL ? min(N, m0 + kBlockQ) : N;
+  const int n_kt = (kend + kTileK - 1) / kTileK;
+  auto stage = [&](int s) { return lds + s * S::STAGE; };
+  auto issue = [&](int it) {
+    uint16_t *st = stage(it & 1);
+    KCopy::issue(Kh, it * kTileK, N, st, kvoff, wave);
+    KCopy::issue(Vh, it * kTileK, N, st + S::TILE, kvoff, wave);
+  };
+  issue(0);
+
+  // Q and dO operands of S^T = K Q^T and dP^T = V dO^T: row my_q, 16kc + 8g ..
+  u32x4 qf[NKC], df[NKC];
+  {
+    const bool ok = my_q < N;
+    const size_t r = (size_t)(ok ? my_q : 0) * D + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      qf[kc] = ok ? *reinterpret_cast<const u32x4 *>(Qh + r + 16 * kc) : u32x4{0, 0, 0, 0};
+      df[kc] = ok ? *reinterpret_cast<const u32x4 *>(dOh + r + 16 * kc) : u32x4{0, 0, 0, 0};
+    }
+  }
+  const f32x2 ldv = my_q < N ? p.ld[(size_t)bh * N + my_q] : f32x2{0.f, 0.f};
+  const float l2 = ldv[0], dd = ldv[1];
+  const TrAddr<D> ta = tr_addr<D>(lane);
+  f32x16 dqt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
+  const float qk = p.qk;
+
+#pragma unroll 1
+  for (int it = 0; it < n_kt; ++it) {
+    if (it + 1 < n_kt) {
+      issue(it + 1);
+      wait_vmcnt<2 * KCopy::INS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    lds_barrier();
+    const uint16_t *kt = stage(it & 1), *vt = kt + S::TILE;
+#pragma unroll
+    for (int kb = 0; kb < kTileK / 32; ++kb) {
+      const int key0 = it * kTileK + 32 * kb;
+      if (CAUSAL && key0 > qw0 + 31) continue;  // every key after every query of this wave
+      // S^T = K Q^T: lane (query my_q) holds keys key0 + 8j + 4g + r in s[4j + r].
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) s = mfma<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) dp = mfma<IS_BF16>(row_frag<D>(vt, 32 * kb + l32, 2 * kc + g), df[kc], dp);
+      const bool edge = (CAUSAL && key0 + 31 > qw0) || key0 + 32 > N;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float x = __builtin_amdgcn_exp2f(s[e] * qk - l2);
+        if (edge) {
+          const int key = key0 + 8 * (e >> 2) + 4 * g + (e & 3);
+          const bool keep = (!CAUSAL || key <= my_q) && key < N;
+          x = keep ? x : 0.f;
+        }
+        dp[e] = x * (dp[e] - dd);  // dS
+      }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 sf = acc_frag<IS_BF16>(dp, t);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          dqt[cb] = mfma<IS_BF16>(tr_frag<D>(kt + 32 * kb * D, ta, t, cb), sf, dqt[cb]);
+      }
+    }
+    lds_barrier();
+  }
+
+  // dQ^T accumulators: lane holds query my_q, columns 32cb + 8j + 4g + 0..3.
+  if (my_q < N) {
+    const size_t row = (size_t)bh * N + my_q;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * cb + 8 * j + 4 * g;
+        const f32x4 q4 = {dqt[cb][4 * j] * p.scale, dqt[cb][4 * j + 1] * p.scale,
+                          dqt[cb][4 * j + 2] * p.scale, dqt[cb][4 * j + 3] * p.scale};
+        if constexpr (GRAD_F32)
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dq) + row * D + c) = q4;
+        else
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dq) + row * D + c) =
+              u32x2{pack2<IS_BF16>(q4[0], q4[1]), pack2<IS_BF16>(q4[2], q4[3])};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+typedef void (*KernelFn)(BwdParams);
+typedef void (*PrepFn)(BwdParams, int64_t);
+
+template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32>
+void pick3(KernelFn &dkdv, KernelFn &dq) {
+  dkdv = bwd_dkdv<D, IS_BF16, CAUSAL, GRAD_F32>;
+  dq = bwd_dq<D, IS_BF16, CAUSAL, GRAD_F32>;
+}
+
+template <int D, bool IS_BF16>
+void pick2(bool causal, bool grad_f32, KernelFn &dkdv, KernelFn &dq) {
+  if (causal) {
+    if (grad_f32) pick3<D, IS_BF16, true, true>(dkdv, dq); else pick3<D, IS_BF16, true, false>(dkdv, dq);
+  } else {
+    if (grad_f32) pick3<D, IS_BF16, false, true>(dkdv, dq); else pick3<D, IS_BF16, false, false>(dkdv, dq);
+  }
+}
+
+template <int D>
+PrepFn pick_prep(bool is_bf16, bool o_f32) {
+  if (is_bf16) return o_f32 ? bwd_prep<D, true, true> : bwd_prep<D, true, false>;
+  return o_f32 ? bwd_prep<D, false, true> : bwd_prep<D, false, false>;
+}
+
+size_t ws_bytes(int64_t B, int64_t H, int64_t N) {
+  return (((size_t)(B * H) * (size_t)N * 8) + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return 0;
+  if (d != 64 && d != 128) return 0;
+  return ws_bytes(B, H, N);
+}
+
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
+                     attn_dtype o_dtype, attn_dtype grad_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  // Validation first: no HIP call happens before every argument is checked.
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+  if (N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+  if (o_dtype != in_dtype && o_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (grad_dtype != in_dtype && grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  const size_t need = ws_bytes(B, H, N);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return ATTN_ERR_WORKSPACE;
+  const int64_t nkb = (N + kBlockK - 1) / kBlockK, nqb = (N + kBlockQ - 1) / kBlockQ;
+  const int64_t rows = B * H * N;
+  const int64_t lpr = d / 8;
+  const int64_t prep_blocks = (rows * lpr + 255) / 256;
+  if (nkb * B * H > INT32_MAX || nqb * B * H > INT32_MAX || prep_blocks > INT32_MAX)
+    return ATTN_ERR_SHAPE;
+
+  BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.ld = reinterpret_cast<f32x2 *>(workspace);
+  p.N = (int)N;
+  p.BH = (int)(B * H);
+  p.qk = (float)((double)scale * 1.4426950408889634);
+  p.scale = scale;
+
+  const bool bf16 = in_dtype == ATTN_BF16, grad_f32 = grad_dtype == ATTN_F32;
+  const bool o_f32 = o_dtype == ATTN_F32;
+  KernelFn fdkdv, fdq;
+  PrepFn fprep;
+  if (d == 64) {
+    fprep = pick_prep<64>(bf16, o_f32);
+    if (bf16) pick2<64, true>(causal != 0, grad_f32, fdkdv, fdq);
+    else pick2<64, false>(causal != 0, grad_f32, fdkdv, fdq);
+  } else {
+    fprep = pick_prep<128>(bf16, o_f32);
+    if (bf16) pick2<128, true>(causal != 0, grad_f32, fdkdv, fdq);
+    else pick2<128, false>(causal != 0, grad_f32, fdkdv, fdq);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  int64_t rows_arg = rows;
+  void *pargs[] = {&p, &rows_arg};
+  hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fprep), dim3((unsigned)prep_blocks),
+                                   dim3(256), pargs, 0, st);
+  void *args[] = {&p};
+  if (err == hipSuccess)
+    err = hipLaunchKernel(reinterpret_cast<const void *>(fdkdv), dim3((unsigned)(nkb * B * H)),
+                          dim3(kThreads), args, 0, st);
+  if (err == hipSuccess)
+    err = hipLaunchKernel(reinterpret_cast<const void *>(fdq), dim3((unsigned)(nqb * B * H)),
+                          dim3(kThreads), args, 0, st);
+  if (err != hipSuccess) {
+    attn_internal::set_last_hip_error((int)err);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

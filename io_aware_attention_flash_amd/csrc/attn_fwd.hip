@@ -1092,6 +1092,12 @@ thread_local int g_last_hip_error = 0;
 
 }  // namespace
 
+// The backward's translation unit reports launch errors through the same
+// per-thread slot that attn_last_hip_error() reads.
+namespace attn_internal {
+void set_last_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace attn_internal
+
 extern "C" {
 
 int attn_abi_version(void) { return ATTN_ABI_VERSION; }
@@ -1106,6 +1112,7 @@ const char *attn_status_string(attn_status s) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype combination";
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
   }
   return "unknown status";
 }

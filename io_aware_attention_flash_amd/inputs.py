@@ -8,6 +8,10 @@ Recipe: a CPU ``torch.Generator`` seeded with ``seed`` draws Q, then K, then
 V, each ``torch.randn(B, H, N, d)`` in fp32; each is multiplied by ``sigma``
 and cast to the workload dtype (round to nearest even). The oracle receives
 these cast values upcast to fp64; the GPU receives them as they are.
+
+The backward's upstream gradient dO is drawn the same way from a generator
+seeded with ``seed + 7919`` (so it is independent of Q, K and V), with
+sigma 1.
 """
 from dataclasses import dataclass
 
@@ -45,6 +49,19 @@ class Workload:
         """Exact lower-triangle count 2*B*H*d*N*(N+1) (causal only)."""
         return 2.0 * self.B * self.H * self.d * self.N * (self.N + 1)
 
+    def bwd_flops(self):
+        """The five N x N x d contractions of the backward (S recomputed, dP,
+        dV, dK, dQ), halved when causal: 2.5x the forward's."""
+        return 2.5 * self.flops()
+
+    def bwd_algorithmic_bytes(self, o_dtype="f32", grad_dtype="f32"):
+        """Read Q, K, V, dO, O and LSE once; write dQ, dK, dV once."""
+        e_in = torch.tensor([], dtype=self.torch_dtype).element_size()
+        e_o = torch.tensor([], dtype=DTYPES[o_dtype]).element_size()
+        e_g = torch.tensor([], dtype=DTYPES[grad_dtype]).element_size()
+        n = self.B * self.H * self.N
+        return (4 * e_in + e_o + 3 * e_g) * n * self.d + 4 * n
+
     def algorithmic_bytes(self, out_dtype=None):
         """Read Q, K, V once; write O (out dtype) and an fp32 LSE per row."""
         e_in = torch.tensor([], dtype=self.torch_dtype).element_size()
@@ -80,6 +97,14 @@ def make_qkv(B, H, N, d, dtype="bf16", sigma=1.0, seed=0):
             x = x * float(sigma)
         out.append(x.to(tdt).contiguous())
     return tuple(out)
+
+
+def make_dout(B, H, N, d, dtype="bf16", seed=0):
+    """Upstream gradient dO for the backward, on the CPU."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    tdt = DTYPES[dtype] if isinstance(dtype, str) else dtype
+    return torch.randn(B, H, N, d, generator=g, dtype=torch.float32).to(tdt).contiguous()
 
 
 def workload_qkv(w: Workload, seed=0):

@@ -58,7 +58,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         s = binding.status_string(code)
         assert isinstance(s, str) and s
     assert binding.status_string(0) == "ok"
@@ -135,3 +135,40 @@ def test_workspace_entry_validates_first(lib, args, code):
                                      a["o"] or None, a["lse"] or None, a["B"], a["H"], a["N"],
                                      a["d"], a["causal"], a["scale"], a["i"], a["o_t"], ws, nbytes)
         assert st == code, (args, ws, st)
+
+
+@pytest.mark.parametrize("B,H,N,d,want", [
+    (2, 32, 4096, 128, 2 * 32 * 4096 * 8),
+    (1, 1, 1, 64, 256),                 # rounded up to 256 bytes
+    (1, 3, 77, 64, 256 * ((3 * 77 * 8 + 255) // 256)),
+    (1, 1, 128, 96, 0), (0, 1, 128, 64, 0), (1, 1, (1 << 24) + 1, 64, 0),
+])
+def test_bwd_workspace_bytes(lib, B, H, N, d, want):
+    assert binding.bwd_workspace_bytes(B, H, N, d) == want
+
+
+@pytest.mark.parametrize("args,code", [
+    # null pointers
+    (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1), (dict(do=0), 1), (dict(dq=0), 1),
+    (dict(dk=0), 1), (dict(dv=0), 1),
+    # shapes
+    (dict(B=0), 2), (dict(N=0), 2), (dict(N=(1 << 24) + 1), 2),
+    # head dims and dtypes: fp32 inputs, O or gradient types outside {in, F32}
+    (dict(d=96), 3), (dict(i=0, o_t=0, g_t=0), 3), (dict(i=2, o_t=1), 3),
+    (dict(i=1, g_t=2), 3), (dict(i=5), 3),
+    # scale
+    (dict(scale=float("nan")), 4), (dict(scale=-1.0), 4),
+    # workspace: missing, too small, misaligned
+    (dict(ws=0), 6), (dict(ws_bytes=100), 6), (dict(ws=P + 8), 6),
+])
+def test_bwd_error_paths_need_no_gpu(lib, args, code):
+    """attn_bwd rejects every bad argument before any HIP call (each case
+    here is invalid, so nothing is launched)."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=1, N=128, d=64,
+             causal=0, scale=0.125, i=2, o_t=0, g_t=0, ws=P, ws_bytes=1 << 20)
+    a.update(args)
+    st = binding.attn_bwd_raw(a["q"] or None, a["k"] or None, a["v"] or None, a["o"] or None,
+                              a["lse"] or None, a["do"] or None, a["dq"] or None, a["dk"] or None,
+                              a["dv"] or None, a["B"], a["H"], a["N"], a["d"], a["causal"],
+                              a["scale"], a["i"], a["o_t"], a["g_t"], a["ws"] or None, a["ws_bytes"])
+    assert st == code, (args, st)

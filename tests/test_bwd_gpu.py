@@ -1,0 +1,301 @@
+"""GPU parity of the backward (attn_bwd): the HIP path against the fp64
+backward oracle on the same seeded inputs.
+
+Tolerance, derived from the arithmetic. The kernels round P and dS once to
+the operand type before each matrix product (unit roundoff u = 2^-8 for
+bf16, 2^-11 for fp16) and accumulate in fp32. An element G = sum_t x_t y_t
+of dQ, dK or dV therefore differs from the exact sum by at most about
+u * T, where T = sum_t |x_t y_t| is the sum of the magnitudes of its terms:
+  dV_jc : T = sum_i P_ij |dO_ic|
+  dK_jc : T = scale sum_i |dS_ij| |q_ic|
+  dQ_ic : T = scale sum_j |dS_ij| |k_jc|
+T is computed in fp64 on the CPU. The test allows
+  |err| <= 2 u T + 1e-5 max|G_ref| + 1e-6.
+The factor 2 covers fp32 rounding and second-order terms. dP - D, a
+difference of two fp32 sums of d products, gets its own allowance of
+d 2^-22 times their magnitudes, and the floor covers elements whose exact
+value is 0. The relative RMS error must also be at most
+u. When the gradients are stored in the input type, u |G_ref| is added for
+the final rounding.
+
+The primary cases give the backward the oracle's O and LSE rounded to fp32,
+so they measure the backward alone. The end-to-end cases use the GPU
+forward's O and LSE, and add the first-order effect of that forward's
+measured error: an error dO_i . dO_err in D_i, or dL_i in LSE_i, moves dS_ij
+by P_ij dD_i or dS_ij dL_i.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_attention_flash_amd import binding
+from io_aware_attention_flash_amd import build as hipbuild
+from io_aware_attention_flash_amd.inputs import WORKLOADS, make_dout, make_qkv
+
+pytestmark = pytest.mark.gpu
+
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def setup_module(module):
+    if not os.path.exists(binding.LIB_PATH):
+        hipbuild.build()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _scale(d):
+    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+
+
+def _inputs(B, H, N, d, dt, sigma, seed):
+    q, k, v = make_qkv(B, H, N, d, dt, sigma, seed=seed)
+    return q, k, v, make_dout(B, H, N, d, dt, seed=seed)
+
+
+def _terms(q, k, v, dout, causal, scale, dD=None, dL=None):
+    """fp64 magnitudes T of the terms of every dQ, dK, dV element (see the
+    module docstring), plus the first-order effect of errors dD and dL in the
+    backward's D and LSE inputs. Used for the tolerance only."""
+    q, k, v, dout = (x.double() for x in (q, k, v, dout))
+    N = q.shape[2]
+    s = (q @ k.transpose(-2, -1).contiguous()) * scale
+    if causal:
+        s = s.masked_fill(~torch.tril(torch.ones(N, N, dtype=torch.bool)), float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    o = p @ v
+    dp = dout @ v.transpose(-2, -1).contiguous()
+    ds = p * (dp - (dout * o).sum(-1, keepdim=True))
+    tq = scale * (ds.abs() @ k.abs())
+    tk = scale * (ds.abs().transpose(-2, -1).contiguous() @ q.abs())
+    tv = p.transpose(-2, -1).contiguous() @ dout.abs()
+    # dP - D is a difference of two fp32 sums of d products each (the matrix
+    # core's and the first pass's): allow d * 2^-22 of their magnitudes.
+    a = dout.abs() @ v.abs().transpose(-2, -1).contiguous() + \
+        (dout.abs() * o.abs()).sum(-1, keepdim=True)
+    e32 = p * a * (q.shape[-1] * 2.0 ** -22)
+    eq = scale * (e32 @ k.abs())
+    ek = scale * (e32.transpose(-2, -1).contiguous() @ q.abs())
+    ev = torch.zeros_like(tv)
+    if dD is not None:
+        dD = dD.double().abs().unsqueeze(-1)
+        eq += scale * dD * (p @ k.abs())
+        ek += scale * (p.transpose(-2, -1).contiguous() @ (dD * q.abs()))
+    if dL is not None:
+        dL = dL.double().abs().unsqueeze(-1)
+        eq += scale * dL * (ds.abs() @ k.abs())
+        ek += scale * ((ds.abs() * dL).transpose(-2, -1).contiguous() @ q.abs())
+        ev += (p * dL).transpose(-2, -1).contiguous() @ dout.abs()
+    return [t.numpy() for t in (tq, tk, tv)], [e.numpy() for e in (eq, ek, ev)]
+
+
+def check_grads(got, ref, terms, extra, u, what, grad_rounding=0.0):
+    for name, g, r, t, e in zip(("dQ", "dK", "dV"), got, ref, terms, extra):
+        g = np.asarray(g, dtype=np.float64)
+        assert np.all(np.isfinite(g)), "%s %s: non-finite" % (what, name)
+        err = np.abs(g - r)
+        tol = 2.0 * u * t + 1.5 * e + grad_rounding * np.abs(r) + 1e-5 * np.abs(r).max() + 1e-6
+        worst = float((err / tol).max())
+        rms = float(np.sqrt((err ** 2).mean()) / max(np.sqrt((r ** 2).mean()), 1e-30))
+        _say("%s %s: max|err| %.2e (max|ref| %.2e) worst err/tol %.3f rel rms %.2e" %
+             (what, name, err.max(), np.abs(r).max(), worst, rms))
+        assert worst <= 1.0, "%s %s: error %.3f times the tolerance" % (what, name, worst)
+        assert rms <= u or np.abs(r).max() == 0.0, "%s %s: relative rms %.2e > u" % (what, name, rms)
+
+
+def gpu_bwd(q, k, v, o, lse, dout, causal, scale, grad_dtype=torch.float32):
+    dev = torch.device("cuda:0")
+    dq, dk, dv = binding.attn_bwd(q.to(dev), k.to(dev), v.to(dev), o.to(dev), lse.to(dev),
+                                  dout.to(dev), causal=causal, scale=scale, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+# ------------------------------------------------------------- full compare
+
+CASES = [
+    # (B, H, N, d, dtype, causal, sigma)
+    (2, 4, 256, 64, "f16", False, 1.0),   # the chapter's own backward test shape
+    (2, 4, 256, 64, "f16", True, 1.0),
+    (1, 2, 1, 64, "bf16", False, 1.0),
+    (1, 2, 1, 128, "f16", True, 1.0),
+    (1, 2, 31, 128, "bf16", True, 1.0),
+    (1, 2, 32, 64, "bf16", True, 1.0),
+    (1, 2, 33, 128, "f16", False, 1.0),
+    (1, 1, 127, 64, "f16", True, 1.0),
+    (1, 2, 128, 128, "bf16", True, 1.0),
+    (1, 2, 129, 128, "bf16", False, 1.0),
+    (1, 3, 200, 64, "bf16", True, 2.0),
+    (2, 1, 255, 128, "f16", True, 1.0),
+    (1, 1, 257, 128, "bf16", True, 1.0),
+    (3, 5, 97, 128, "bf16", False, 1.0),
+    (1, 2, 300, 128, "bf16", True, 1.0),
+    (1, 1, 513, 64, "f16", False, 1.0),
+    (1, 1, 1000, 128, "bf16", True, 3.0),
+    (2, 8, 160, 128, "bf16", True, 1.0),
+    (1, 16, 70, 64, "f16", False, 1.0),
+]
+
+
+def _case_id(c):
+    return "B%dH%dN%dd%d_%s_%s_s%g" % (c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full",
+                                      c[6])
+
+
+def _oracle_o_lse(q, k, v, causal, scale):
+    ro, rl = oracle.attn_oracle(q, k, v, causal=causal, scale=scale)
+    return torch.from_numpy(ro).float(), torch.from_numpy(rl).float()
+
+
+@pytest.mark.parametrize("case", CASES, ids=_case_id)
+def test_bwd_matches_oracle(case):
+    """Backward alone: O and LSE are the oracle's, rounded to fp32."""
+    B, H, N, d, dt, causal, sigma = case
+    _say("case", _case_id(case))
+    q, k, v, dout = _inputs(B, H, N, d, dt, sigma, seed=11)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, causal, scale)
+    got = gpu_bwd(q, k, v, o, lse, dout, causal, scale)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    terms, extra = _terms(q, k, v, dout, causal, scale)
+    check_grads(got, ref, terms, extra, U[dt], _case_id(case))
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[8], CASES[14], CASES[16]],
+                         ids=_case_id)
+def test_bwd_end_to_end(case):
+    """GPU forward then GPU backward, against the oracle's exact gradients;
+    the tolerance adds the first-order effect of the forward's measured
+    O and LSE errors."""
+    B, H, N, d, dt, causal, sigma = case
+    _say("case", _case_id(case))
+    q, k, v, dout = _inputs(B, H, N, d, dt, sigma, seed=12)
+    scale = _scale(d)
+    dev = torch.device("cuda:0")
+    o, lse = binding.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=causal, scale=scale,
+                              out_dtype=torch.float32)
+    got = gpu_bwd(q, k, v, o, lse, dout, causal, scale)
+    ro, rl = oracle.attn_oracle(q, k, v, causal=causal, scale=scale)
+    dD = (dout.double() * (o.cpu().double() - torch.from_numpy(ro))).sum(-1)
+    dL = lse.cpu().double() - torch.from_numpy(rl)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    terms, extra = _terms(q, k, v, dout, causal, scale, dD=dD, dL=dL)
+    check_grads(got, ref, terms, extra, U[dt], "end-to-end " + _case_id(case))
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[9], CASES[10]], ids=_case_id)
+def test_bwd_input_dtype_o_and_grads(case):
+    """O handed over in the input type (rounded, so D moves by up to
+    u sum_c |dO_ic O_ic|) and gradients stored in the input type."""
+    B, H, N, d, dt, causal, sigma = case
+    _say("case", _case_id(case))
+    q, k, v, dout = _inputs(B, H, N, d, dt, sigma, seed=13)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, causal, scale)
+    o_in = o.to(DT[dt])
+    got = gpu_bwd(q, k, v, o_in, lse, dout, causal, scale, grad_dtype=DT[dt])
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    dD = U[dt] * (dout.double().abs() * o.double().abs()).sum(-1)
+    terms, extra = _terms(q, k, v, dout, causal, scale, dD=dD)
+    check_grads([g.float() for g in got], ref, terms, extra, U[dt], _case_id(case) + " in-dtype",
+                grad_rounding=U[dt])
+
+
+def test_bwd_exercise5_embedded():
+    """Exercise 5 ("4.4 Writing GPU Kernels with Triton", section
+    "Exercises") differentiated in closed form, embedded at d = 64 in fp16
+    (every value exact): q = e0, keys 2 e0 and 4 e0, values e0 and 3 e0,
+    scale 1, upstream gradient e0 on the query that sees both keys."""
+    import json
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden",
+                                    "exercise5_online_softmax.json")))
+    p1, p2 = g["weights"]
+    o_ex = g["O_normalised"]
+    d = 64
+    q = torch.zeros(1, 1, 2, d, dtype=torch.float16)
+    k = torch.zeros_like(q)
+    v = torch.zeros_like(q)
+    dout = torch.zeros_like(q)
+    q[0, 0, :, 0] = 1.0
+    k[0, 0, :, 0] = torch.tensor(g["scores"])
+    v[0, 0, :, 0] = torch.tensor(g["values"])
+    dout[0, 0, 1, 0] = 1.0
+    o, lse = _oracle_o_lse(q, k, v, False, 1.0)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, dout, False, 1.0)
+    (k1, k2), (v1, v2) = g["scores"], g["values"]
+    tol = 4 * U["f16"] * 8  # largest term magnitudes here are below 8
+    assert abs(dq[0, 0, 1, 0].item() - p1 * p2 * (v2 - v1) * (k2 - k1)) <= tol
+    assert abs(dk[0, 0, 0, 0].item() - p1 * (v1 - o_ex)) <= tol
+    assert abs(dk[0, 0, 1, 0].item() - p2 * (v2 - o_ex)) <= tol
+    assert abs(dv[0, 0, 0, 0].item() - p1) <= tol and abs(dv[0, 0, 1, 0].item() - p2) <= tol
+    assert torch.count_nonzero(dq[0, 0, 0]) == 0 and torch.count_nonzero(dq[0, 0, 1, 1:]) == 0
+
+
+def test_bwd_deterministic():
+    """No atomics: two calls give the same bits."""
+    q, k, v, dout = _inputs(1, 4, 700, 128, "bf16", 1.0, seed=14)
+    scale = _scale(128)
+    o, lse = _oracle_o_lse(q, k, v, True, scale)
+    a = gpu_bwd(q, k, v, o, lse, dout, True, scale)
+    b = gpu_bwd(q, k, v, o, lse, dout, True, scale)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+# ------------------------------------------------ full-size, sampled rows
+
+FULL = ["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_bwd_full_size_sampled(name):
+    """The full workloads (GPU forward then backward, as a training step
+    would run them): sampled query rows (dQ) and key rows (dK, dV) of two
+    heads against the oracle, plus the Jacobian invariants on every head:
+    the dK rows of a head sum to 0 and the dV rows to the dO rows' sum."""
+    w = WORKLOADS[name]
+    _say("workload", name)
+    q, k, v = make_qkv(w.B, w.H, w.N, w.d, w.dtype, w.sigma, seed=0)
+    dout = make_dout(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+    dev = torch.device("cuda:0")
+    o, lse = binding.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=w.causal, scale=w.scale,
+                              out_dtype=torch.float32)
+    dq, dk, dv = binding.attn_bwd(q.to(dev), k.to(dev), v.to(dev), o, lse, dout.to(dev),
+                                  causal=w.causal, scale=w.scale, grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    u = U[w.dtype]
+    for x in (dq, dk, dv):
+        assert bool(torch.isfinite(x).all())
+    # invariants on every head (fp64 sums on the GPU of the fp32 gradients)
+    sk = dk.double().sum(2)
+    sv = dv.double().sum(2) - dout.to(dev).double().sum(2)
+    mag_k = dk.double().abs().sum(2)
+    mag_v = dv.double().abs().sum(2)
+    assert bool((sk.abs() <= 16 * u * mag_k + 1e-4).all()), "dK rows do not sum to 0"
+    assert bool((sv.abs() <= 16 * u * mag_v + 1e-4).all()), "dV rows do not sum to sum dO"
+    # sampled rows of two heads
+    rng = np.random.default_rng(0)
+    N = w.N
+    heads = [0, w.B * w.H - 1]
+    for bh in heads:
+        b, h = divmod(bh, w.H)
+        rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, N // 2, N - 2, N - 1],
+                                         rng.integers(0, N, 7)]))
+        qh, kh, vh, dh = (x[b:b + 1, h:h + 1] for x in (q, k, v, dout))
+        rq, rk, rv = oracle.attn_bwd_oracle(qh, kh, vh, dh, causal=w.causal, scale=w.scale,
+                                            qrows=rows, krows=rows)
+        ro, rl = oracle.attn_oracle(qh, kh, vh, causal=w.causal, scale=w.scale)
+        dD = (dh.double() * (o[b:b + 1, h:h + 1].cpu().double() - torch.from_numpy(ro))).sum(-1)
+        dL = lse[b:b + 1, h:h + 1].cpu().double() - torch.from_numpy(rl)
+        terms, extra = _terms(qh, kh, vh, dh, w.causal, w.scale, dD=dD, dL=dL)
+        got = [dq[b, h].cpu()[rows], dk[b, h].cpu()[rows], dv[b, h].cpu()[rows]]
+        terms = [t[0, 0][rows] for t in terms]
+        extra = [e[0, 0][rows] for e in extra]
+        check_grads(got, (rq, rk, rv), terms, extra, u, "%s head %d" % (name, bh))
