@@ -1,7 +1,7 @@
 """Benchmark of the attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--out-dtype f32|in] [--no-cpu-baseline]
+                    [--out-dtype f32|in] [--no-cpu-baseline] [--pass fwd|bwd]
 
 A step is one attn_fwd call (the whole forward: QK^T, masking, online
 softmax, P.V, normalisation, LSE) over one batch of seeded synthetic input
@@ -18,6 +18,12 @@ right after a short warm-up lands in that dip and reads about 15% slow.
 Prints one JSON line. FLOPs count the two N x N x d contractions per head,
 halved when causal: 4*B*H*N^2*d (/2). Algorithmic bytes read Q, K, V once
 and write O and LSE once.
+
+--pass bwd times the backward instead (one attn_bwd call per step, all of
+its launches, with O and LSE from one untimed forward). Its FLOPs count the
+five contractions of the backward (S recomputed, dP, dV, dK, dQ), 2.5x the
+forward's; the atomic-free split recomputes S and dP in its dQ kernel, so it
+executes 1.4x that count.
 """
 import argparse
 import hashlib
@@ -33,7 +39,7 @@ sys.path.insert(0, ROOT)
 
 from io_aware_attention_flash_amd import binding  # noqa: E402
 from io_aware_attention_flash_amd import build as hipbuild  # noqa: E402
-from io_aware_attention_flash_amd.inputs import HEADLINE, WORKLOADS, workload_qkv  # noqa: E402
+from io_aware_attention_flash_amd.inputs import HEADLINE, WORKLOADS, make_dout, workload_qkv  # noqa: E402
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
@@ -87,6 +93,97 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
             "seconds": round(elapsed, 3)}
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, budget_s=12.0):
+    """Time the fp64 backward oracle (dQ of every row, dK and dV of every key)
+    on whole heads of the same inputs until about `budget_s` seconds."""
+    import oracle
+    oracle.build_oracle()
+    threads = oracle.oracle_threads()
+    B, H, N, d = q.shape
+    heads_done, elapsed = 0, 0.0
+    for bh in range(B * H):
+        b, h = divmod(bh, H)
+        args = [x[b:b + 1, h:h + 1] for x in (q, k, v, dout)]
+        t0 = time.perf_counter()
+        oracle.attn_bwd_oracle(*args, causal=w.causal, scale=w.scale)
+        elapsed += time.perf_counter() - t0
+        heads_done += 1
+        if elapsed >= budget_s:
+            break
+    flops = w.bwd_flops() * heads_done / (B * H)
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d heads of %s (fp64 backward oracle, %.1f s; rate on the "
+                      "backward's five-contraction FLOP count)" % (heads_done, B * H, w.name, elapsed),
+            "seconds": round(elapsed, 3)}
+
+
+def bench_bwd(args):
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    if w.dtype not in ("bf16", "f16"):
+        print("the backward supports bf16 and fp16 inputs only", file=sys.stderr)
+        sys.exit(2)
+    qc, kc, vc = workload_qkv(w, seed=0)
+    dc = make_dout(w.B, w.H, w.N, w.d, w.dtype, seed=0)
+    q, k, v, dout = qc.to(dev), kc.to(dev), vc.to(dev), dc.to(dev)
+    o, lse = binding.attn_fwd(q, k, v, causal=w.causal, scale=w.scale, out_dtype=torch.float32)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+    ws = torch.empty(binding.bwd_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        binding.attn_bwd(q, k, v, o, lse, dout, causal=w.causal, scale=w.scale,
+                         grad_dtype=torch.float32, workspace=ws, grads=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    flops = w.bwd_flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    alg_bytes = w.bwd_algorithmic_bytes("f32", "f32")
+    res = {
+        "metric": "attention bwd TFLOP/s (five contractions%s)" % (", causal halved" if w.causal else ""),
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0, sigma^2) Q/K/V, N(0, 1) dO)",
+        "config": {"workload": w.name, "pass": "bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "in_dtype": w.dtype, "o_dtype": "f32", "grad_dtype": "f32",
+                   "sigma": w.sigma, "scale": w.scale},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None,
+                     "scope": "whole attn_bwd call (prep + dK/dV + dQ launches)"},
+        "hbm": {"algorithmic_bytes": alg_bytes,
+                "achieved_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+                "peak_GBps": PEAK_HBM_GBS},
+        "wall_s_timed_region": round(wall, 4),
+        "flops_per_step": flops,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_bwd(w, qc, kc, vc, dc, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +192,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "in"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="time the forward (default) or the backward")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (reference "
@@ -118,6 +217,9 @@ def main():
     if not os.path.exists(binding.LIB_PATH):
         hipbuild.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.which == "bwd":
+        bench_bwd(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

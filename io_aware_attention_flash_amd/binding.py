@@ -166,13 +166,14 @@ def bwd_workspace_bytes(B, H, N, d):
     return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
 
 
-def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, workspace=None):
+def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, workspace=None,
+             grads=None):
     """Attention backward on the current HIP stream: (dq, dk, dv) for the
     upstream gradient dout, given the forward's inputs, its output o (input
     dtype or float32) and its lse. grad_dtype defaults to the input dtype
     (torch.float32 is also accepted). The workspace (a uint8 tensor of at
     least bwd_workspace_bytes(...) bytes) is taken from torch's allocator when
-    not given.
+    not given. Preallocated (dq, dk, dv) may be passed as `grads`.
     """
     if q.dim() != 4 or any(x.shape != q.shape for x in (k, v, o, dout)):
         raise ValueError("q, k, v, o, dout must all be [B, H, N, d] of one shape")
@@ -194,7 +195,12 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
     grad_dtype = grad_dtype or q.dtype
     if grad_dtype not in (q.dtype, torch.float32):
         raise ValueError("grad_dtype must be the input dtype or float32")
-    dq, dk, dv = (torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3))
+    if grads is None:
+        grads = [torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3)]
+    dq, dk, dv = grads
+    if any(g.shape != q.shape or g.dtype != grad_dtype or not g.is_contiguous() or
+           g.device != q.device for g in grads):
+        raise ValueError("grads must be contiguous [B, H, N, d] tensors of grad_dtype on q's device")
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
