@@ -1,0 +1,24 @@
+"""The torch operators (ops.py) on a host without a GPU: they register under
+their namespace and their fake implementations give the right shapes, so
+torch's tracing can see through them."""
+import torch
+from torch._subclasses.fake_tensor import FakeTensorMode
+
+import io_aware_attention_flash_amd as pkg
+from io_aware_attention_flash_amd import ops  # noqa: F401  (registers the ops)
+
+
+def test_ops_are_registered():
+    assert hasattr(torch.ops.io_aware_attention_flash, "fwd")
+    assert hasattr(torch.ops.io_aware_attention_flash, "bwd")
+    assert callable(pkg.flash_attn_func)
+
+
+def test_fake_shapes():
+    with FakeTensorMode():
+        q = torch.empty(2, 3, 17, 64, dtype=torch.bfloat16)
+        o, lse = torch.ops.io_aware_attention_flash.fwd(q, q, q, True, 0.125)
+        assert o.shape == q.shape and o.dtype == q.dtype
+        assert lse.shape == (2, 3, 17) and lse.dtype == torch.float32
+        dq, dk, dv = torch.ops.io_aware_attention_flash.bwd(q, q, q, o, lse, q, True, 0.125)
+        assert dq.shape == dk.shape == dv.shape == q.shape
