@@ -176,6 +176,36 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                      attn_dtype o_dtype, attn_dtype grad_dtype, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * attn_fwd_strided -- the attention forward of attn_fwd for general layouts:
+ * Nq query rows against Nk keys per head (cross-attention; the pages'
+ * "Triton Kernel Practice" checks its kernel on mismatched query and key
+ * lengths), any head dimension d = 8, 16, ..., 128 (computed at 64 or 128
+ * with zero-padded columns, exact by "4.4 Writing GPU Kernels with Triton",
+ * section "Sizing the attention kernel"), and strided tensors.
+ *
+ * q          : device, element (b, h, i, c) at q + b*qs[0] + h*qs[1] + i*qs[2] + c
+ *              (elements of in_dtype) for i < Nq, c < d; likewise k and v
+ *              with Nk rows, and o (out_dtype) with Nq rows; written.
+ * *_strides  : three int64 element strides (b, h, row), or NULL for the
+ *              contiguous [B][H][n][d] layout. The column stride is 1. Each
+ *              pointer and stride*element size must be a multiple of 16
+ *              bytes, strides non-negative, the row stride >= d, and every
+ *              offset below 2^47 elements; for bf16/fp16, 64 rows of K or V
+ *              must span less than 2^31 bytes. Otherwise ATTN_ERR_UNSUPPORTED.
+ * lse        : device, [B][H][Nq] contiguous fp32; written.
+ * causal     : requires Nq == Nk (else ATTN_ERR_SHAPE).
+ * d          : a multiple of 8 in [8, 128] (else ATTN_ERR_UNSUPPORTED).
+ * Other arguments, dtype pairs, precision, errors and ownership are those of
+ * attn_fwd. Results equal attn_fwd's within the forward's tolerance, not
+ * bitwise: a separate, simpler kernel computes them.
+ */
+attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void *k,
+                             const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                             void *o, const int64_t *o_strides, float *lse, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                             attn_dtype in_dtype, attn_dtype out_dtype, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(attn_status s);
 

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
           4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE"}
-EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_bwd",
+EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_fwd_strided", "attn_bwd",
            "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version",
            "attn_last_hip_error")
 
@@ -48,6 +48,11 @@ def load_library(path=LIB_PATH):
                                 ctypes.c_float, ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.attn_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, ctypes.c_int]
+    i64p = ctypes.POINTER(i64)
+    lib.attn_fwd_strided.restype = ctypes.c_int
+    lib.attn_fwd_strided.argtypes = [vp, i64p, vp, i64p, vp, i64p, vp, i64p, vp, i64, i64, i64, i64,
+                                     i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                     vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
@@ -85,6 +90,69 @@ def attn_fwd_ws_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, N, d, causal, sca
                                       int(out_dtype), ws_ptr, int(ws_bytes), stream)
 
 
+def _strides(st):
+    return None if st is None else (ctypes.c_int64 * 3)(*[int(x) for x in st])
+
+
+def attn_fwd_strided_raw(q_ptr, q_st, k_ptr, k_st, v_ptr, v_st, o_ptr, o_st, lse_ptr, B, H, Nq,
+                         Nk, d, causal, scale, in_dtype, out_dtype, stream=None):
+    """Direct call of attn_fwd_strided; *_st are (b, h, row) element strides
+    or None (contiguous). Returns the status."""
+    return load_library().attn_fwd_strided(q_ptr, _strides(q_st), k_ptr, _strides(k_st), v_ptr,
+                                           _strides(v_st), o_ptr, _strides(o_st), lse_ptr,
+                                           int(B), int(H), int(Nq), int(Nk), int(d),
+                                           int(bool(causal)), float(scale), int(in_dtype),
+                                           int(out_dtype), stream)
+
+
+def needs_general(q, k, v):
+    """Whether a call needs the general-layout kernel (attn_fwd_strided):
+    different query and key lengths, a head dim other than 64 or 128, or
+    tensors that are not contiguous [B, H, N, d]."""
+    return (k.shape[2] != q.shape[2] or q.shape[3] not in (64, 128) or
+            not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()))
+
+
+def attn_fwd_general(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=None):
+    """Attention forward through attn_fwd_strided: q [B, H, Nq, d], k and v
+    [B, H, Nk, d], any strides with a unit column stride and 16-byte aligned
+    rows, d a multiple of 8 up to 128. `out` may be a strided [B, H, Nq, d]
+    view; lse is [B, H, Nq] contiguous."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape or \
+            (q.shape[0], q.shape[1], q.shape[3]) != (k.shape[0], k.shape[1], k.shape[3]):
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_TO_ATTN:
+        raise ValueError("q, k, v must share one dtype among float32/float16/bfloat16")
+    if not (q.is_cuda and k.device == q.device and v.device == q.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if any(x.stride(3) != 1 for x in (q, k, v)):
+        raise ValueError("the last dimension must be contiguous")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / d ** 0.5
+    out_dtype = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != out_dtype or out.stride(3) != 1 or out.device != q.device:
+        raise ValueError("out must be a [B, H, Nq, d] tensor of out_dtype with a unit last stride")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, H, Nq] float32 tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_strided_raw(q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3],
+                              v.data_ptr(), v.stride()[:3], out.data_ptr(), out.stride()[:3],
+                              lse.data_ptr(), B, H, Nq, Nk, d, causal, scale,
+                              _TORCH_TO_ATTN[q.dtype], _TORCH_TO_ATTN[out_dtype], stream)
+    if st != 0:
+        msg = status_string(st)
+        if st == 5:
+            msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
+        raise AttnError(st, msg)
+    return out, lse
+
+
 def workspace_bytes(B, H, N, d, in_dtype):
     """Bytes of device workspace attn_fwd_ws can use for this problem (0: none)."""
     return int(load_library().attn_fwd_workspace_bytes(int(B), int(H), int(N), int(d),
@@ -95,6 +163,9 @@ def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=No
              workspace=None):
     """Attention forward of [B, H, N, d] tensors on the current HIP stream.
 
+    Calls that need the general-layout kernel (different key length, a head
+    dim other than 64 or 128, strided tensors) go to attn_fwd_general.
+
     scale defaults to 1/sqrt(d); out_dtype defaults to the input dtype
     (torch.float32 is also accepted for bf16/fp16 inputs). Returns (o, lse)
     with lse [B, H, N] fp32 natural-log logsumexp. Preallocated `out`/`lse`
@@ -103,6 +174,10 @@ def attn_fwd(q, k, v, causal=False, scale=None, out_dtype=None, out=None, lse=No
     workspace_bytes(...) bytes may be passed as `workspace`; otherwise one is
     taken from torch's allocator for the call.
     """
+    if q.dim() == 4 and k.dim() == 4 and needs_general(q, k, v) and \
+            (out is None or out.stride(3) == 1):
+        return attn_fwd_general(q, k, v, causal=causal, scale=scale, out_dtype=out_dtype, out=out,
+                                lse=lse)
     if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
         raise ValueError("q, k, v must all be [B, H, N, d] of one shape")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in _TORCH_TO_ATTN:

@@ -1,7 +1,7 @@
 """Build libattn_fwd.so (the gfx950 HIP kernels and the C ABI) in-tree.
 
-The library holds the forward (csrc/attn_fwd.hip) and the backward
-(csrc/attn_bwd.hip).
+The library holds the forward (csrc/attn_fwd.hip), the backward
+(csrc/attn_bwd.hip) and the general-layout forward (csrc/attn_general.hip).
 
     python -m io_aware_attention_flash_amd.build
 
@@ -18,7 +18,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", "attn_fwd.hip"), os.path.join(PKG, "csrc", "attn_bwd.hip")]
+SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_general.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")

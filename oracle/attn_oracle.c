@@ -41,8 +41,9 @@
 #define ORACLE_BAD_ARG 1
 #define ORACLE_NO_MEMORY 2
 
-/* One query row: row `i` of head `bh`. q,k,v point at the head's [N][d]
- * matrices. `s` is scratch of N doubles. */
+/* One query row: row `i` of head `bh`. q points at the head's [Nq][d]
+ * queries, k and v at its [N][d] keys and values (N keys). `s` is scratch
+ * of N doubles. */
 static void oracle_one_row(const double *q, const double *k, const double *v,
                            int64_t N, int64_t d, int causal, double scale,
                            int64_t i, double *s, double *o_row, double *lse) {
@@ -77,22 +78,28 @@ static void oracle_one_row(const double *q, const double *k, const double *v,
 }
 
 /*
- * attn_oracle_rows -- attention for a list of query rows.
+ * attn_oracle_rows_qk -- attention for a list of query rows, with Nq query
+ * rows and Nk keys per head (cross-attention when they differ; the
+ * "Triton Kernel Practice" page validates its kernel on such shapes). The
+ * causal mask (query i sees keys j <= i) is defined here for Nq == Nk only.
  *
- * q, k, v  : [B][H][N][d] row-major fp64 (callers upcast the exact values
- *            the GPU receives).
- * rows     : flat row ids r = (b*H + h)*N + i, or NULL for every row in order.
+ * q        : [B][H][Nq][d] row-major fp64;  k, v : [B][H][Nk][d] (callers
+ *            upcast the exact values the GPU receives).
+ * rows     : flat query row ids r = (b*H + h)*Nq + i, or NULL for every row.
  * o        : [nrows][d] fp64 out;  lse : [nrows] fp64 out (natural log).
  * nthreads : OpenMP threads (<= 0: the runtime default).
- * Returns ORACLE_OK, or ORACLE_BAD_ARG for a bad size or row id.
+ * Returns ORACLE_OK, or ORACLE_BAD_ARG for a bad size, row id or a causal
+ * mask with Nq != Nk.
  */
-int attn_oracle_rows(const double *q, const double *k, const double *v,
-                     int64_t B, int64_t H, int64_t N, int64_t d, int causal,
-                     double scale, const int64_t *rows, int64_t nrows,
-                     double *o, double *lse, int nthreads) {
+int attn_oracle_rows_qk(const double *q, const double *k, const double *v,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        double scale, const int64_t *rows, int64_t nrows,
+                        double *o, double *lse, int nthreads) {
   if (!q || !k || !v || !o || !lse) return ORACLE_BAD_ARG;
-  if (B < 1 || H < 1 || N < 1 || d < 1 || nrows < 0) return ORACLE_BAD_ARG;
-  const int64_t total = B * H * N;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nrows < 0) return ORACLE_BAD_ARG;
+  if (causal && Nq != Nk) return ORACLE_BAD_ARG;
+  const int64_t N = Nk;
+  const int64_t total = B * H * Nq;
   if (!rows && nrows != total) return ORACLE_BAD_ARG;
   if (rows) {
     for (int64_t r = 0; r < nrows; ++r)
@@ -113,9 +120,10 @@ int attn_oracle_rows(const double *q, const double *k, const double *v,
 #endif
       for (int64_t r = 0; r < nrows; ++r) {
         const int64_t flat = rows ? rows[r] : r;
-        const int64_t bh = flat / N, i = flat % N;
+        const int64_t bh = flat / Nq, i = flat % Nq;
+        const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;
         const size_t head = (size_t)bh * (size_t)N * (size_t)d;
-        oracle_one_row(q + head, k + head, v + head, N, d, causal, scale, i, s,
+        oracle_one_row(q + qhead, k + head, v + head, N, d, causal, scale, i, s,
                        o + r * d, lse + r);
       }
       free(s);
@@ -123,6 +131,15 @@ int attn_oracle_rows(const double *q, const double *k, const double *v,
   }
   (void)nthreads;
   return bad_alloc ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* attn_oracle_rows -- the same with Nq = Nk = N (self-attention). */
+int attn_oracle_rows(const double *q, const double *k, const double *v,
+                     int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                     double scale, const int64_t *rows, int64_t nrows,
+                     double *o, double *lse, int nthreads) {
+  return attn_oracle_rows_qk(q, k, v, B, H, N, N, d, causal, scale, rows, nrows, o, lse,
+                             nthreads);
 }
 
 /* Threads an OpenMP region of this library would use by default. */

@@ -60,6 +60,10 @@ def open_oracle_library(path):
     lib.attn_oracle_rows.argtypes = [dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
                                      ctypes.c_double, ctypes.POINTER(i64), i64,
                                      dp, dp, ctypes.c_int]
+    lib.attn_oracle_rows_qk.restype = ctypes.c_int
+    lib.attn_oracle_rows_qk.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                        ctypes.c_double, ctypes.POINTER(i64), i64,
+                                        dp, dp, ctypes.c_int]
     lib.attn_oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -103,7 +107,8 @@ def _as_f64(x):
 
 
 def attn_oracle(q, k, v, causal=False, scale=None, rows=None, nthreads=0, lib=None):
-    """fp64 attention of [B,H,N,d] inputs.
+    """fp64 attention of [B,H,Nq,d] queries over [B,H,Nk,d] keys and values
+    (Nq and Nk may differ when not causal).
 
     scale: the softmax scale; None means 1/sqrt(d). Pass the exact value the
            GPU path receives (e.g. the fp32 number) to compare like for like.
@@ -113,9 +118,11 @@ def attn_oracle(q, k, v, causal=False, scale=None, rows=None, nthreads=0, lib=No
            pins catch planted mistakes); default: this package's build.
     """
     q, k, v = _as_f64(q), _as_f64(k), _as_f64(v)
-    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
-        raise ValueError("q, k, v must share one [B,H,N,d] shape")
+    if q.ndim != 4 or k.ndim != 4 or v.shape != k.shape or k.shape[:2] + k.shape[3:] != \
+            q.shape[:2] + q.shape[3:]:
+        raise ValueError("q [B,H,Nq,d] and k, v [B,H,Nk,d] must agree in B, H and d")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     lib = lib or _load()
@@ -131,9 +138,16 @@ def attn_oracle(q, k, v, causal=False, scale=None, rows=None, nthreads=0, lib=No
         rows_ptr = rows_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
         o = np.empty((nrows, d), dtype=np.float64)
         lse = np.empty((nrows,), dtype=np.float64)
-    st = lib.attn_oracle_rows(q.ctypes.data_as(dp), k.ctypes.data_as(dp), v.ctypes.data_as(dp),
-                              B, H, N, d, int(bool(causal)), float(scale), rows_ptr, nrows,
-                              o.ctypes.data_as(dp), lse.ctypes.data_as(dp), int(nthreads))
+    if Nk == N:
+        st = lib.attn_oracle_rows(q.ctypes.data_as(dp), k.ctypes.data_as(dp),
+                                  v.ctypes.data_as(dp), B, H, N, d, int(bool(causal)),
+                                  float(scale), rows_ptr, nrows, o.ctypes.data_as(dp),
+                                  lse.ctypes.data_as(dp), int(nthreads))
+    else:
+        st = lib.attn_oracle_rows_qk(q.ctypes.data_as(dp), k.ctypes.data_as(dp),
+                                     v.ctypes.data_as(dp), B, H, N, Nk, d, int(bool(causal)),
+                                     float(scale), rows_ptr, nrows, o.ctypes.data_as(dp),
+                                     lse.ctypes.data_as(dp), int(nthreads))
     if st != 0:
         raise RuntimeError("attn_oracle_rows failed with status %d" % st)
     return o, lse

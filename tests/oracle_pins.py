@@ -252,10 +252,49 @@ def check_row_subset(attn):
         _close(ls_, lse.reshape(-1)[rows], 0.0, "row subset LSE")
 
 
+def check_cross_attention(attn):
+    """Query and key lengths that differ ("Triton Kernel Practice" validates
+    its kernel on Q (5, 32) against K, V (15, 32) and on a single query
+    against 10 keys): agreement with torch's fp64 scaled_dot_product_attention
+    and with the brute-force two-pass and online variants, at the page's
+    shapes and a few more."""
+    shapes = [(1, 1, 5, 15, 32), (1, 1, 1, 10, 64), (2, 3, 7, 40, 16), (1, 2, 33, 3, 8)]
+    for t, (B, H, nq, nk, d) in enumerate(shapes):
+        q = _rand((B, H, nq, d), 200 + t)
+        k, v = _rand((B, H, nk, d), 210 + t), _rand((B, H, nk, d), 220 + t)
+        scale = 1.0 / np.sqrt(d)
+        o, lse = attn(q, k, v, False, scale)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale).numpy()
+        ref_l = torch.logsumexp((tq @ tk.transpose(-2, -1)) * scale, dim=-1).numpy()
+        _close(o, ref, 1e-12, "cross-attention vs sdpa %s" % (shapes[t],))
+        _close(lse, ref_l, 1e-12, "cross-attention LSE %s" % (shapes[t],))
+        o2, l2 = attn_two_pass_np(q[0, 0], k[0, 0], v[0, 0], False, scale)
+        _close(o[0, 0], o2, 1e-12, "cross-attention two-pass")
+        o3, l3 = attn_online_np(q[0, 0], k[0, 0], v[0, 0], False, scale, block=4)
+        _close(o[0, 0], o3, 1e-12, "cross-attention online")
+        _close(lse[0, 0], l3, 1e-12, "cross-attention online LSE")
+
+
+def check_cross_rows_independent(attn):
+    """Each query row attends on its own: the rows of a cross-attention
+    batch equal single-query calls, and row subsets equal the full result."""
+    q, k, v = _rand((1, 2, 9, 8), 230), _rand((1, 2, 21, 8), 231), _rand((1, 2, 21, 8), 232)
+    o, lse = attn(q, k, v, False, 0.4)
+    for i in (0, 4, 8):
+        oi, li = attn(q[:, :, i:i + 1], k, v, False, 0.4)
+        _close(oi[:, :, 0], o[:, :, i], 1e-15, "single query row %d" % i)
+        _close(li[:, :, 0], lse[:, :, i], 1e-15, "single query LSE %d" % i)
+    rows = [17, 0, 9, 3]
+    os_, ls_ = attn(q, k, v, False, 0.4, rows=rows)
+    _close(os_, o.reshape(-1, 8)[rows], 0.0, "cross-attention row subset")
+
+
 ALL_CHECKS = [
     check_exercise5, check_weights_sum_to_one, check_weights_identity_v,
     check_constant_scores, check_single_key, check_causal_first_and_last_row,
     check_prefix_consistency, check_variants_agree, check_torch_library,
     check_shift_invariance, check_key_permutation, check_linearity_and_hull,
     check_head_dim_zero_padding, check_large_logits, check_row_subset,
+    check_cross_attention, check_cross_rows_independent,
 ]

@@ -172,3 +172,27 @@ def test_bwd_error_paths_need_no_gpu(lib, args, code):
                               a["dv"] or None, a["B"], a["H"], a["N"], a["d"], a["causal"],
                               a["scale"], a["i"], a["o_t"], a["g_t"], a["ws"] or None, a["ws_bytes"])
     assert st == code, (args, st)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), 1), (dict(v=0), 1), (dict(lse=0), 1),
+    (dict(Nq=0), 2), (dict(Nk=0), 2), (dict(causal=1, Nk=64), 2),
+    (dict(d=0), 3), (dict(d=4), 3), (dict(d=100), 3), (dict(d=136), 3),
+    (dict(i=0, o_t=2), 3), (dict(i=2, o_t=1), 3),
+    (dict(q=P + 8), 3),                                   # misaligned base
+    (dict(q_st=(-4096, 4096, 64)), 3),                    # negative stride
+    (dict(k_st=(1 << 20, 1 << 14, 32)), 3),               # row stride < d
+    (dict(v_st=(1 << 20, 1 << 14, 68)), 3),               # row not 16-byte aligned (bf16)
+    (dict(scale=float("nan")), 4),
+])
+def test_strided_error_paths_need_no_gpu(lib, args, code):
+    """attn_fwd_strided rejects every bad argument before any HIP call (each
+    case here is invalid, so nothing is launched)."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, q_st=None, k_st=None, v_st=None, o_st=None, B=1, H=2,
+             Nq=32, Nk=48, d=64, causal=0, scale=0.125, i=2, o_t=0)
+    a.update(args)
+    st = binding.attn_fwd_strided_raw(a["q"] or None, a["q_st"], a["k"] or None, a["k_st"],
+                                      a["v"] or None, a["v_st"], a["o"] or None, a["o_st"],
+                                      a["lse"] or None, a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                      a["causal"], a["scale"], a["i"], a["o_t"])
+    assert st == code, (args, st)

@@ -1,0 +1,138 @@
+"""GPU parity of the general-layout forward (attn_fwd_strided): cross-attention,
+head dims other than 64 / 128 and strided tensors, against the fp64 oracle
+on the same seeded inputs. Tolerances are the forward's: O max |err| <= 1e-2
+and mean |err| <= 1e-3 (fp32 output), LSE max |err| <= 1e-3."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_attention_flash_amd import binding
+from io_aware_attention_flash_amd import build as hipbuild
+from io_aware_attention_flash_amd.inputs import make_qkv
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_MAX = 1e-2, 1e-3, 1e-3
+DEV = torch.device("cuda:0")
+
+
+def setup_module(module):
+    if not os.path.exists(binding.LIB_PATH):
+        hipbuild.build()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _scale(d):
+    return float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+
+
+def _qkv(B, H, Nq, Nk, d, dt, sigma, seed):
+    q = make_qkv(B, H, Nq, d, dt, sigma, seed=seed)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dt, sigma, seed=seed + 1)
+    return q, k, v
+
+
+def _check(o, lse, q, k, v, causal, scale, what):
+    ro, rl = oracle.attn_oracle(q, k, v, causal=causal, scale=scale)
+    err = np.abs(o.detach().cpu().double().numpy() - ro)
+    lerr = np.abs(lse.detach().cpu().double().numpy() - rl)
+    print("%s: O max %.3e mean %.3e | LSE max %.3e" % (what, err.max(), err.mean(), lerr.max()),
+          flush=True)
+    assert np.all(np.isfinite(err)) and np.all(np.isfinite(lerr)), what
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN and lerr.max() <= LSE_MAX, what
+
+
+CROSS = [
+    # (B, H, Nq, Nk, d, dtype, sigma): the page's two shapes first
+    (1, 1, 5, 15, 32, "f32", 1.0), (1, 1, 1, 10, 64, "f32", 1.0),
+    (1, 1, 5, 15, 32, "bf16", 1.0), (1, 1, 1, 10, 64, "f16", 1.0),
+    (2, 3, 300, 77, 128, "bf16", 1.0), (1, 2, 64, 1000, 64, "f16", 1.0),
+    (1, 1, 129, 257, 128, "bf16", 3.0), (2, 2, 1, 1, 8, "f16", 1.0),
+    (1, 2, 200, 130, 96, "f32", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: "B%dH%dNq%dNk%dd%d_%s_s%g" % c)
+def test_cross_attention(case):
+    B, H, Nq, Nk, d, dt, sigma = case
+    print("case", case, flush=True)
+    q, k, v = _qkv(B, H, Nq, Nk, d, dt, sigma, seed=31)
+    scale = _scale(d)
+    o, lse = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(o, lse, q, k, v, False, scale, "cross %s" % (case,))
+
+
+HEAD_DIMS = [(8, "bf16", False), (32, "f16", True), (48, "bf16", True), (72, "f16", False),
+             (80, "bf16", True), (96, "f16", True), (112, "bf16", False), (24, "f32", True)]
+
+
+@pytest.mark.parametrize("d,dt,causal", HEAD_DIMS)
+def test_head_dims(d, dt, causal):
+    print("case d", d, dt, causal, flush=True)
+    for (B, H, N) in ((1, 2, 100), (2, 1, 300)):
+        q, k, v = make_qkv(B, H, N, d, dt, 1.0, seed=32)
+        scale = _scale(d)
+        o, lse = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale,
+                                  out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _check(o, lse, q, k, v, causal, scale, "d=%d %s causal=%s N=%d" % (d, dt, causal, N))
+
+
+@pytest.mark.parametrize("dt,causal", [("bf16", True), ("f16", False), ("f32", True)])
+def test_strided_layouts(dt, causal):
+    """Q, K, V from a [B, N, H, d] projection (strides (N H d, d, H d)); V a
+    column slice of a wider tensor (row stride > d); O written into a
+    [B, N, H, d] buffer through its transposed view."""
+    B, H, N, d = 2, 3, 190, 80
+    print("case strided", dt, causal, flush=True)
+    g = torch.Generator().manual_seed(33)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dt]
+    qkv = torch.randn(B, N, 3, H, d, generator=g).to(tdt)
+    wide = torch.randn(B, H, N, 128, generator=g).to(tdt)
+    q, k = qkv[:, :, 0].transpose(1, 2), qkv[:, :, 1].transpose(1, 2)
+    v = wide[..., :d]
+    scale = _scale(d)
+    qkv_g = qkv.to(DEV)
+    qg, kg = qkv_g[:, :, 0].transpose(1, 2), qkv_g[:, :, 1].transpose(1, 2)
+    vg = wide.to(DEV)[..., :d]
+    assert not (qg.is_contiguous() or kg.is_contiguous() or vg.is_contiguous())
+    obuf = torch.zeros(B, N, H, d, dtype=torch.float32, device=DEV)
+    o, lse = binding.attn_fwd(qg, kg, vg, causal=causal, scale=scale, out_dtype=torch.float32,
+                              out=obuf.transpose(1, 2))
+    torch.cuda.synchronize()
+    assert o.data_ptr() == obuf.data_ptr()
+    _check(obuf.transpose(1, 2), lse, q.contiguous(), k.contiguous(), v.contiguous(), causal,
+           scale, "strided %s causal=%s" % (dt, causal))
+
+
+@pytest.mark.parametrize("d,dt,causal", [(128, "bf16", True), (64, "f16", False)])
+def test_general_kernel_on_fast_shapes(d, dt, causal):
+    """attn_fwd_strided on contiguous shapes the tuned kernels also take:
+    both within the forward's tolerance of the oracle."""
+    B, H, N = 2, 2, 513
+    q, k, v = make_qkv(B, H, N, d, dt, 1.0, seed=34)
+    scale = _scale(d)
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    o, lse = binding.attn_fwd_general(qg, kg, vg, causal=causal, scale=scale,
+                                      out_dtype=torch.float32)
+    o2, lse2 = binding.attn_fwd(qg, kg, vg, causal=causal, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _check(o, lse, q, k, v, causal, scale, "general d=%d" % d)
+    _check(o2, lse2, q, k, v, causal, scale, "tuned d=%d" % d)
+
+
+def test_input_dtype_output():
+    """bf16 output of a cross-attention call: within 1e-2 plus half an ulp."""
+    q, k, v = _qkv(1, 2, 150, 260, 96, "bf16", 1.0, seed=35)
+    scale = _scale(96)
+    o, lse = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.bfloat16
+    ro, _ = oracle.attn_oracle(q, k, v, causal=False, scale=scale)
+    err = np.abs(o.cpu().double().numpy() - ro)
+    assert np.all(err <= 1e-2 + 0.5 * np.abs(ro) * 2.0 ** -8 + 1e-30)

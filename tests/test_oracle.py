@@ -42,6 +42,13 @@ def test_online_variant_reproduces_exercise5_state():
     assert abs(lse[0] - g["lse"]) <= 1e-15
 
 
+def test_oracle_rejects_causal_cross_attention():
+    """The causal mask is defined for equal query and key lengths only."""
+    with pytest.raises(RuntimeError):
+        oracle.attn_oracle(np.zeros((1, 1, 3, 2)), np.zeros((1, 1, 5, 2)), np.zeros((1, 1, 5, 2)),
+                           causal=True)
+
+
 def test_oracle_rejects_bad_rows():
     q = np.zeros((1, 1, 4, 2))
     with pytest.raises(RuntimeError):

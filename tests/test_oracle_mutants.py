@@ -33,6 +33,9 @@ MUTANTS = {
     "last_key_dropped_from_output": [("for (int64_t j = 0; j < n_keys; ++j) {\n    const double w",
                                       "for (int64_t j = 0; j + 1 < n_keys; ++j) {\n    const double w")],
     "last_key_dropped_from_sum": [("    l += s[j];", "    l += (j + 1 < n_keys) ? s[j] : 0.0;")],
+    "query_head_uses_key_length": [("const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;",
+                                    "const size_t qhead = (size_t)bh * (size_t)N * (size_t)d;")],
+    "keys_counted_with_query_length": [("  const int64_t N = Nk;\n", "  const int64_t N = Nk < Nq ? Nk : Nq;\n")],
     "query_row_off_by_one": [("const double *qi = q + i * d;",
                               "const double *qi = q + ((i + 1) % N) * d;")],
 }
