@@ -184,6 +184,53 @@ def bench_bwd(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_general(args):
+    """The general-layout kernel (attn_fwd_strided) on the workload's shape,
+    with Q, K, V as [B, N, H, d] tensors seen through [B, H, N, d] views (the
+    layout a fused projection produces) and O written the same way."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOADS[args.workload]
+    qc, kc, vc = workload_qkv(w, seed=0)
+    q, k, v = (x.to(dev).transpose(1, 2).contiguous().transpose(1, 2) for x in (qc, kc, vc))
+    assert not q.is_contiguous()
+    obuf = torch.empty((w.B, w.N, w.H, w.d), dtype=torch.float32, device=dev)
+    o = obuf.transpose(1, 2)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+    def step():
+        binding.attn_fwd_general(q, k, v, causal=w.causal, scale=w.scale, out_dtype=torch.float32,
+                                 out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    tflops = w.flops() / (ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    res = {"metric": "attention fwd TFLOP/s, general-layout kernel", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded N(0, sigma^2) Q/K/V)",
+           "config": {"workload": w.name, "pass": "fwd_general", "layout": "BNHD views",
+                      "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                      "in_dtype": w.dtype, "out_dtype": "f32"},
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                        "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+           "wall_s_timed_region": round(wall, 4), "flops_per_step": w.flops()}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -192,8 +239,9 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "in"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
-                    help="time the forward (default) or the backward")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "fwd_general"],
+                    help="time the forward (default), the backward, or the general-layout "
+                         "forward on [B, N, H, d] views")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (reference "
@@ -219,6 +267,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.which == "bwd":
         bench_bwd(args)
+        return
+    if args.which == "fwd_general":
+        bench_general(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
