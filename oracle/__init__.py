@@ -12,6 +12,9 @@ Contents
   attn_bwd_oracle(q, k, v, dout, causal, scale, qrows=None, krows=None) -> (dQ, dK, dV)
       fp64 attention gradients in C (``attn_bwd_oracle.c``), written out from
       their definitions; dQ per query row, dK and dV per key row.
+  row_softmax(x) -> y
+      fp64 three-pass row softmax of an M x N matrix (``softmax.py``), the
+      pages' Kernel 2.
   attn_two_pass_np / attn_online_np
       tiny pure-NumPy fp64 variants used to pin the C oracle (brute force on
       small inputs); see ``variants.py``.
@@ -23,3 +26,4 @@ from .native import (attn_oracle, oracle_threads, build_oracle, compile_oracle, 
                      open_oracle_library, library_path, attn_bwd_oracle,
                      open_bwd_oracle_library, bwd_library_path)
 from .variants import attn_two_pass_np, attn_online_np  # noqa: F401
+from .softmax import row_softmax  # noqa: F401
