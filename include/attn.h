@@ -206,6 +206,25 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
                              int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
                              attn_dtype in_dtype, attn_dtype out_dtype, void *stream);
 
+/*
+ * attn_row_softmax -- y_ij = exp(x_ij - max_j x_ij) / sum_j exp(x_ij - max_j x_ij)
+ * for every row i of an M x N matrix: the fused softmax of "4.4 Writing GPU
+ * Kernels with Triton", section "Kernel 2: Fused Softmax", reading each row
+ * once and writing it once (rows longer than 16384 are read twice).
+ *
+ * x : device, row i at x + i * x_row_stride (elements of in_dtype), N values.
+ * y : device, row i at y + i * y_row_stride (elements of out_dtype); written.
+ * in_dtype / out_dtype : (F32, F32), (BF16, BF16), (BF16, F32), (F16, F16),
+ *     (F16, F32). Arithmetic is fp32.
+ * Limits: 1 <= M < 2^31, 1 <= N <= 2^30, N <= row strides <= 2^40, pointers
+ * aligned to their element size (else ATTN_ERR_SHAPE / ATTN_ERR_UNSUPPORTED).
+ * Rows whose every value is -inf give NaN, as the definition does.
+ * Errors, ownership and the stream: as for attn_fwd. y must not overlap x.
+ */
+attn_status attn_row_softmax(const void *x, int64_t x_row_stride, void *y, int64_t y_row_stride,
+                             int64_t M, int64_t N, attn_dtype in_dtype, attn_dtype out_dtype,
+                             void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *attn_status_string(attn_status s);
 

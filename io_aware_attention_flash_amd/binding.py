@@ -17,7 +17,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
           4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_fwd_strided", "attn_bwd",
-           "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version",
+           "attn_bwd_workspace_bytes", "attn_row_softmax", "attn_status_string", "attn_abi_version",
            "attn_last_hip_error")
 
 _TORCH_TO_ATTN = {torch.float32: ATTN_F32, torch.float16: ATTN_F16, torch.bfloat16: ATTN_BF16}
@@ -53,6 +53,8 @@ def load_library(path=LIB_PATH):
     lib.attn_fwd_strided.argtypes = [vp, i64p, vp, i64p, vp, i64p, vp, i64p, vp, i64, i64, i64, i64,
                                      i64, ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                      vp]
+    lib.attn_row_softmax.restype = ctypes.c_int
+    lib.attn_row_softmax.argtypes = [vp, i64, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
@@ -291,3 +293,34 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
             msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
         raise AttnError(st, msg)
     return dq, dk, dv
+
+
+def row_softmax_raw(x_ptr, xs, y_ptr, ys, M, N, in_dtype, out_dtype, stream=None):
+    """Direct call of attn_row_softmax; returns the status."""
+    return load_library().attn_row_softmax(x_ptr, int(xs), y_ptr, int(ys), int(M), int(N),
+                                           int(in_dtype), int(out_dtype), stream)
+
+
+def row_softmax(x, out_dtype=None, out=None):
+    """Softmax over the last dimension of a 2-D GPU tensor x (rows may be
+    strided; the last dimension must be contiguous), into a new tensor or
+    into `out`."""
+    if x.dim() != 2 or not x.is_cuda or x.dtype not in _TORCH_TO_ATTN or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D float32/float16/bfloat16 GPU tensor with unit column "
+                         "stride")
+    M, N = x.shape
+    out_dtype = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    if out.shape != x.shape or out.dtype != out_dtype or out.stride(1) != 1 or \
+            out.device != x.device:
+        raise ValueError("out must be an M x N tensor of out_dtype with unit column stride")
+    st = row_softmax_raw(x.data_ptr(), x.stride(0), out.data_ptr(), out.stride(0), M, N,
+                         _TORCH_TO_ATTN[x.dtype], _TORCH_TO_ATTN[out_dtype],
+                         torch.cuda.current_stream(x.device).cuda_stream)
+    if st != 0:
+        msg = status_string(st)
+        if st == 5:
+            msg += " (hipError_t %d)" % load_library().attn_last_hip_error()
+        raise AttnError(st, msg)
+    return out

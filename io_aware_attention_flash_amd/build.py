@@ -1,7 +1,8 @@
 """Build libattn_fwd.so (the gfx950 HIP kernels and the C ABI) in-tree.
 
 The library holds the forward (csrc/attn_fwd.hip), the backward
-(csrc/attn_bwd.hip) and the general-layout forward (csrc/attn_general.hip).
+(csrc/attn_bwd.hip), the general-layout forward (csrc/attn_general.hip) and
+the row softmax (csrc/softmax.hip).
 
     python -m io_aware_attention_flash_amd.build
 
@@ -18,7 +19,8 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRCS = [os.path.join(PKG, "csrc", n) for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_general.hip")]
+SRCS = [os.path.join(PKG, "csrc", n)
+        for n in ("attn_fwd.hip", "attn_bwd.hip", "attn_general.hip", "softmax.hip")]
 LIB = os.path.join(PKG, "libattn_fwd.so")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = os.environ.get("ATTN_OFFLOAD_ARCH", "gfx950")

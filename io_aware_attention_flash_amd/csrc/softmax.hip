@@ -1,0 +1,271 @@
+// Row softmax for gfx950 (MI355X): y_ij = exp(x_ij - max_j x_ij) / sum_j
+// exp(x_ij - max_j x_ij) over every row of an M x N matrix -- the fused
+// softmax of "4.4 Writing GPU Kernels with Triton", section "Kernel 2: Fused
+// Softmax": each row is read from HBM once and written once, with the
+// maximum, the exponentials and the sum formed on chip.
+//
+// The kernel is bound by HBM. A row of up to 4096 columns belongs to one
+// wave (four rows per workgroup) and lives in its registers, so the
+// reductions are wave-wide (DPP/permute, no LDS); a row of up to 16384
+// columns belongs to a workgroup of four waves and the reductions add one
+// LDS exchange; longer rows take two passes (an online maximum and sum,
+// then the normalised write: two reads and one write). Loads are 16-byte
+// vectors when the row pointers, the strides and N allow it, and coalesced
+// element loads otherwise. Arithmetic is fp32; the exponential is
+// v_exp_f32 on x * log2(e) - max * log2(e).
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn_internal {
+void set_last_hip_error(int e);
+}
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct SmParams {
+  const void *x;
+  void *y;
+  int64_t xs, ys;  // row strides (elements)
+  int M, N;
+};
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T v);
+template <>
+__device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <>
+__device__ __forceinline__ float to_f32<__bf16>(__bf16 v) { return (float)v; }
+template <>
+__device__ __forceinline__ float to_f32<_Float16>(_Float16 v) { return (float)v; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float v) { return (T)v; }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Reduction over the WPR waves that share a row (WPR = 1: the wave alone).
+template <int WPR, bool IS_MAX>
+__device__ __forceinline__ float row_reduce(float v, float *red, int wave) {
+  v = IS_MAX ? wave_max(v) : wave_sum(v);
+  if constexpr (WPR > 1) {
+    __syncthreads();  // the previous use of `red` is over
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) r = IS_MAX ? fmaxf(r, red[w]) : r + red[w];
+    v = r;
+  }
+  return v;
+}
+
+// Rows held in registers: VPL values per lane, WPR waves per row (64 * WPR
+// lanes), N <= 64 * WPR * VPL. VEC: each lane moves 16-byte pieces (CH
+// values), piece k of lane t at columns (k * 64 * WPR + t) * CH; otherwise
+// value k of lane t is column k * 64 * WPR + t.
+template <typename TIN, typename TOUT, int WPR, int VPL, bool VEC>
+__global__ __launch_bounds__(kThreads) void softmax_rows(SmParams p) {
+  constexpr int ROWS = 4 / WPR;  // rows per workgroup
+  constexpr int T = 64 * WPR;    // lanes per row
+  constexpr int CH = 16 / sizeof(TIN);
+  constexpr int NP = VEC ? VPL / CH : 0;  // 16-byte pieces per lane
+  static_assert(!VEC || NP * CH == VPL, "whole pieces");
+  __shared__ float red[4];
+  const int wave = threadIdx.x >> 6;
+  const int sub = wave / WPR;               // row of this workgroup
+  const int t = threadIdx.x - sub * T;      // lane within the row
+  const int64_t row = (int64_t)blockIdx.x * ROWS + sub;
+  const bool live = row < p.M;              // uniform per wave
+  const int N = p.N;
+  const TIN *xr = static_cast<const TIN *>(p.x) + (live ? row : 0) * p.xs;
+  TOUT *yr = static_cast<TOUT *>(p.y) + (live ? row : 0) * p.ys;
+
+  float v[VPL];
+  if constexpr (VEC) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int c0 = (k * T + t) * CH;
+      union { u32x4 w; TIN e[CH]; } u;
+      u.w = live && c0 < N ? *reinterpret_cast<const u32x4 *>(xr + c0) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < CH; ++e) v[k * CH + e] = live && c0 < N ? to_f32<TIN>(u.e[e]) : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int c = k * T + t;
+      v[k] = live && c < N ? to_f32<TIN>(xr[c]) : -INFINITY;
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) m = fmaxf(m, v[k]);
+  m = row_reduce<WPR, true>(m, red, wave) * kLog2e;
+  float l = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    v[k] = __builtin_amdgcn_exp2f(fmaf(v[k], kLog2e, -m));  // exp(-inf) = 0 for padding
+    l += v[k];
+  }
+  l = row_reduce<WPR, false>(l, red, wave);
+  const float inv = 1.0f / l;
+  if (!live) return;
+  if constexpr (VEC) {
+    constexpr int OCH = 16 / sizeof(TOUT);  // output values per 16 bytes
+    static_assert(CH % OCH == 0, "input piece covers whole output pieces");
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int c0 = (k * T + t) * CH;
+      if (c0 >= N) continue;
+#pragma unroll
+      for (int s = 0; s < CH / OCH; ++s) {
+        union { u32x4 w; TOUT e[OCH]; } u;
+#pragma unroll
+        for (int e = 0; e < OCH; ++e) u.e[e] = from_f32<TOUT>(v[k * CH + s * OCH + e] * inv);
+        *reinterpret_cast<u32x4 *>(yr + c0 + s * OCH) = u.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) {
+      const int c = k * T + t;
+      if (c < N) yr[c] = from_f32<TOUT>(v[k] * inv);
+    }
+  }
+}
+
+// Long rows: one workgroup per row, two passes. Pass 1 keeps a running
+// maximum and a running sum per thread (rescaled when the maximum grows),
+// pass 2 re-reads the row and writes the normalised values.
+template <typename TIN, typename TOUT>
+__global__ __launch_bounds__(kThreads) void softmax_long(SmParams p) {
+  __shared__ float red[4];
+  const int wave = threadIdx.x >> 6;
+  const int64_t row = blockIdx.x;
+  const int N = p.N;
+  const TIN *xr = static_cast<const TIN *>(p.x) + row * p.xs;
+  TOUT *yr = static_cast<TOUT *>(p.y) + row * p.ys;
+  float m = -INFINITY, l = 0.f;
+  for (int c = threadIdx.x; c < N; c += kThreads) {
+    const float x = to_f32<TIN>(xr[c]) * kLog2e;
+    if (x > m) {
+      l = l * __builtin_amdgcn_exp2f(m - x) + 1.f;  // 0 * ... when m was -inf
+      m = x;
+    } else if (x != -INFINITY) {
+      l += __builtin_amdgcn_exp2f(x - m);
+    }
+  }
+  const float mr = row_reduce<4, true>(m, red, wave);
+  l = l * (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mr));
+  const float inv = 1.0f / row_reduce<4, false>(l, red, wave);
+  for (int c = threadIdx.x; c < N; c += kThreads)
+    yr[c] = from_f32<TOUT>(__builtin_amdgcn_exp2f(fmaf(to_f32<TIN>(xr[c]), kLog2e, -mr)) * inv);
+}
+
+typedef void (*SmFn)(SmParams);
+
+template <typename TIN, typename TOUT, int WPR, bool VEC>
+SmFn pick_vpl(int vpl) {
+  switch (vpl) {
+    case 8: return softmax_rows<TIN, TOUT, WPR, 8, VEC>;
+    case 16: return softmax_rows<TIN, TOUT, WPR, 16, VEC>;
+    case 32: return softmax_rows<TIN, TOUT, WPR, 32, VEC>;
+    default: return softmax_rows<TIN, TOUT, WPR, 64, VEC>;
+  }
+}
+
+template <typename TIN, typename TOUT>
+SmFn pick_kernel(int wpr, int vpl, bool vec, bool longrow) {
+  if (longrow) return softmax_long<TIN, TOUT>;
+  if (wpr == 1) return vec ? pick_vpl<TIN, TOUT, 1, true>(vpl) : pick_vpl<TIN, TOUT, 1, false>(vpl);
+  return vec ? pick_vpl<TIN, TOUT, 4, true>(vpl) : pick_vpl<TIN, TOUT, 4, false>(vpl);
+}
+
+SmFn pick(attn_dtype in, attn_dtype out, int wpr, int vpl, bool vec, bool longrow) {
+  if (in == ATTN_F32) return pick_kernel<float, float>(wpr, vpl, vec, longrow);
+  if (in == ATTN_BF16)
+    return out == ATTN_F32 ? pick_kernel<__bf16, float>(wpr, vpl, vec, longrow)
+                           : pick_kernel<__bf16, __bf16>(wpr, vpl, vec, longrow);
+  return out == ATTN_F32 ? pick_kernel<_Float16, float>(wpr, vpl, vec, longrow)
+                         : pick_kernel<_Float16, _Float16>(wpr, vpl, vec, longrow);
+}
+
+int esize(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_row_softmax(const void *x, int64_t x_row_stride, void *y, int64_t y_row_stride,
+                             int64_t M, int64_t N, attn_dtype in_dtype, attn_dtype out_dtype,
+                             void *stream) {
+  if (!x || !y) return ATTN_ERR_NULL;
+  if (M < 1 || N < 1 || M > INT32_MAX || N > (int64_t(1) << 30)) return ATTN_ERR_SHAPE;
+  if (x_row_stride < N || y_row_stride < N || x_row_stride > (int64_t(1) << 40) ||
+      y_row_stride > (int64_t(1) << 40))
+    return ATTN_ERR_SHAPE;
+  const bool in_ok = in_dtype == ATTN_F32 || in_dtype == ATTN_F16 || in_dtype == ATTN_BF16;
+  if (!in_ok) return ATTN_ERR_UNSUPPORTED;
+  if (out_dtype != in_dtype && out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  const int ei = esize(in_dtype), eo = esize(out_dtype);
+  if ((reinterpret_cast<uintptr_t>(x) % ei) != 0 || (reinterpret_cast<uintptr_t>(y) % eo) != 0)
+    return ATTN_ERR_UNSUPPORTED;
+  // 16-byte pieces when every row starts 16-byte aligned and N is whole pieces
+  const int ch = 16 / ei;
+  const bool vec = (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (x_row_stride * ei) % 16 == 0 &&
+                   (y_row_stride * eo) % 16 == 0 && N % ch == 0;
+  int wpr = 1, vpl = 8;
+  bool longrow = false;
+  if (N <= 64 * 64) {
+    wpr = 1;
+  } else if (N <= 256 * 64) {
+    wpr = 4;
+  } else {
+    longrow = true;
+  }
+  if (!longrow) {
+    const int64_t lanes = 64 * wpr;
+    while ((int64_t)vpl * lanes < N) vpl *= 2;
+  }
+  SmParams p;
+  p.x = x;
+  p.y = y;
+  p.xs = x_row_stride;
+  p.ys = y_row_stride;
+  p.M = (int)M;
+  p.N = (int)N;
+  const int64_t rows_per_wg = longrow ? 1 : 4 / wpr;
+  const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
+  SmFn fn = pick(in_dtype, out_dtype, wpr, vpl, vec, longrow);
+  void *args[] = {&p};
+  const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
+                                         dim3(kThreads), args, 0, (hipStream_t)stream);
+  if (err != hipSuccess) {
+    attn_internal::set_last_hip_error((int)err);
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

@@ -196,3 +196,18 @@ def test_strided_error_paths_need_no_gpu(lib, args, code):
                                       a["lse"] or None, a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
                                       a["causal"], a["scale"], a["i"], a["o_t"])
     assert st == code, (args, st)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(x=0), 1), (dict(y=0), 1),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(xs=10), 2), (dict(ys=10), 2),
+    (dict(N=(1 << 30) + 1, xs=(1 << 31), ys=(1 << 31)), 2),
+    (dict(i=0, o=2), 3), (dict(i=2, o=1), 3), (dict(i=7, o=7), 3),
+    (dict(x=P + 1), 3),                          # not aligned to its element size
+])
+def test_row_softmax_error_paths_need_no_gpu(lib, args, code):
+    a = dict(x=P, xs=64, y=P, ys=64, M=4, N=64, i=2, o=2)
+    a.update(args)
+    st = binding.row_softmax_raw(a["x"] or None, a["xs"], a["y"] or None, a["ys"], a["M"], a["N"],
+                                 a["i"], a["o"])
+    assert st == code, (args, st)

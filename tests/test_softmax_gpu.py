@@ -1,0 +1,97 @@
+"""GPU parity of attn_row_softmax against the fp64 oracle (the pages' Kernel 2).
+
+Tolerance from the arithmetic: fp32 throughout (exp on v_exp_f32, one
+reciprocal per row), so each output is within a few fp32 roundings of the
+exact value relative to its size: |err| <= 1e-5 |y| + 1e-7 (the page reports
+~1e-7 absolute on its test). Outputs stored in bf16/fp16 add their rounding:
+the unit roundoff u |y| (2^-8 bf16, 2^-11 fp16), and half the fp16 subnormal
+spacing. Inputs are the seeded draws rounded to the input dtype; the
+oracle receives the same rounded values."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_attention_flash_amd import binding
+from io_aware_attention_flash_amd import build as hipbuild
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+# Rounding to the output type: at most the unit roundoff u times |y| (RNE),
+# plus half the subnormal spacing for fp16 (outputs below 2^-14).
+ROUND = {"f32": 2.0 ** -24, "bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+SUBNORMAL = {"f32": 0.0, "bf16": 0.0, "f16": 2.0 ** -25}
+
+
+def setup_module(module):
+    if not os.path.exists(binding.LIB_PATH):
+        hipbuild.build()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _x(M, N, dt, sigma, seed):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(M, N, generator=g) * sigma).to(DT[dt])
+
+
+def _check(y, x, out, what):
+    ref = oracle.row_softmax(x)
+    got = y.cpu().double().numpy()
+    err = np.abs(got - ref)
+    tol = 1e-5 * np.abs(ref) + 1e-7 + ROUND[out] * np.abs(ref) + SUBNORMAL[out]
+    worst = float((err / tol).max())
+    print("%s: max|err| %.2e worst err/tol %.3f" % (what, err.max(), worst), flush=True)
+    assert np.all(np.isfinite(got)) and worst <= 1.0, what
+
+
+SHAPES = [
+    # (M, N, dtype, sigma): the page's test shape and the 2000-column bug case first
+    (1823, 781, "f32", 1.0), (4, 5, "f32", 1.0), (3, 2000, "f32", 1.0),
+    (7, 1, "bf16", 1.0), (33, 63, "f16", 2.0), (64, 512, "bf16", 1.0),
+    (17, 4096, "bf16", 3.0), (9, 4097, "f16", 1.0), (5, 16384, "f32", 1.0),
+    (3, 16385, "bf16", 1.0), (2, 70001, "f16", 1.0), (300, 1024, "f16", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", SHAPES, ids=lambda c: "M%dN%d_%s_s%g" % c)
+def test_row_softmax(case):
+    M, N, dt, sigma = case
+    print("case", case, flush=True)
+    x = _x(M, N, dt, sigma, seed=41)
+    for out in sorted({dt, "f32"}):
+        y = binding.row_softmax(x.to(DEV), out_dtype=DT[out])
+        torch.cuda.synchronize()
+        _check(y, x, out, "%s -> %s" % (case, out))
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_strided_rows(dt):
+    """Rows further apart than N (a column slice of a wider matrix), with odd
+    N (element loads) and with N a multiple of the 16-byte piece."""
+    for N, pad in ((781, 13), (1024, 64)):
+        x = _x(40, N, dt, 1.0, seed=42)
+        xg = torch.zeros(40, N + pad, dtype=DT[dt], device=DEV)
+        xg[:, :N] = x.to(DEV)
+        xv = xg[:, :N]
+        ybuf = torch.zeros(40, N + 8, dtype=DT[dt], device=DEV)
+        y = binding.row_softmax(xv, out=ybuf[:, :N])
+        torch.cuda.synchronize()
+        _check(y, x, dt, "strided N=%d pad=%d %s" % (N, pad, dt))
+        assert torch.count_nonzero(ybuf[:, N:]) == 0, "wrote past the row"
+
+
+def test_large_logits_and_inf():
+    """Entries of -inf get 0, a dominant entry gets 1, and +-1e4 shifts do
+    not overflow."""
+    x = torch.zeros(3, 300)
+    x[0, 7] = 1e4
+    x[1, :] = -1e4
+    x[1, 5] = 0.0
+    x[2, 100:] = float("-inf")
+    y = binding.row_softmax(x.to(DEV)).cpu()
+    assert y[0, 7].item() == 1.0 and torch.count_nonzero(y[0]) == 1
+    assert y[1, 5].item() == 1.0
+    assert torch.all(y[2, 100:] == 0) and abs(y[2, :100].sum().item() - 1.0) <= 1e-6
