@@ -231,6 +231,60 @@ def bench_general(args):
     print(json.dumps(res), flush=True)
 
 
+def bench_softmax(args):
+    """attn_row_softmax on an M x N matrix (HBM-bound: one read, one write)."""
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, N = args.sm_rows, args.sm_cols
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[args.sm_dtype]
+    g = torch.Generator().manual_seed(0)
+    xc = torch.randn(M, N, generator=g).to(tdt)
+    x = xc.to(dev)
+    y = torch.empty_like(x)
+
+    def step():
+        binding.row_softmax(x, out=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    nbytes = 2 * M * N * x.element_size()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"metric": "row softmax HBM GB/s (one read + one write)", "value": round(gbs, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": args.sm_dtype, "data": "synthetic (seeded N(0, 1))",
+           "config": {"workload": "row_softmax_m%d_n%d_%s" % (M, N, args.sm_dtype),
+                      "pass": "softmax", "M": M, "N": N},
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+           "wall_s_timed_region": round(wall, 4), "bytes_per_step": nbytes}
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 0
+        t1 = time.perf_counter()
+        while rows < M and time.perf_counter() - t1 < args.cpu_budget:
+            oracle.row_softmax(xc[rows:rows + 256])
+            rows += min(256, M - rows)
+        el = time.perf_counter() - t1
+        res["cpu_baseline"] = {"value": 2 * rows * N * x.element_size() / el / 1e9, "unit": "GB/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": "%d of %d rows (fp64 NumPy oracle, %.1f s)" % (rows, M, el),
+                               "seconds": round(el, 3)}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,9 +293,13 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, choices=sorted(WORKLOADS))
     ap.add_argument("--out-dtype", default="f32", choices=["f32", "in"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "fwd_general"],
-                    help="time the forward (default), the backward, or the general-layout "
-                         "forward on [B, N, H, d] views")
+    ap.add_argument("--pass", dest="which", default="fwd",
+                    choices=["fwd", "bwd", "fwd_general", "softmax"],
+                    help="time the forward (default), the backward, the general-layout "
+                         "forward on [B, N, H, d] views, or the row softmax")
+    ap.add_argument("--sm-rows", type=int, default=32768)
+    ap.add_argument("--sm-cols", type=int, default=4096)
+    ap.add_argument("--sm-dtype", default="bf16", choices=["f32", "bf16", "f16"])
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (reference "
@@ -270,6 +328,9 @@ def main():
         return
     if args.which == "fwd_general":
         bench_general(args)
+        return
+    if args.which == "softmax":
+        bench_softmax(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

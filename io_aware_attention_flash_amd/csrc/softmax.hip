@@ -6,10 +6,10 @@
 //
 // The kernel is bound by HBM. A row of up to 4096 columns belongs to one
 // wave (four rows per workgroup) and lives in its registers, so the
-// reductions are wave-wide (DPP/permute, no LDS); a row of up to 16384
-// columns belongs to a workgroup of four waves and the reductions add one
-// LDS exchange; longer rows take two passes (an online maximum and sum,
-// then the normalised write: two reads and one write). Loads are 16-byte
+// reductions are wave-wide (no LDS); a row of up to 16384 or 65536 columns
+// belongs to a workgroup of 4 or 16 waves and the reductions add one LDS
+// exchange; longer rows take two passes (an online maximum and sum, then the
+// normalised write: two reads and one write). Loads are 16-byte
 // vectors when the row pointers, the strides and N allow it, and coalesced
 // element loads otherwise. Arithmetic is fp32; the exponential is
 // v_exp_f32 on x * log2(e) - max * log2(e).
@@ -28,7 +28,6 @@ void set_last_hip_error(int e);
 
 namespace {
 
-constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct SmParams {
@@ -61,7 +60,8 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Reduction over the WPR waves that share a row (WPR = 1: the wave alone).
+// Reduction over the WPR waves that share a row (WPR = 1: the wave alone;
+// otherwise the workgroup is that one row).
 template <int WPR, bool IS_MAX>
 __device__ __forceinline__ float row_reduce(float v, float *red, int wave) {
   v = IS_MAX ? wave_max(v) : wave_sum(v);
@@ -77,18 +77,23 @@ __device__ __forceinline__ float row_reduce(float v, float *red, int wave) {
   return v;
 }
 
+// Threads per workgroup of the register-resident kernel: four one-wave rows,
+// or one row of 4 or 16 waves.
+template <int WPR>
+constexpr int rows_threads() { return WPR == 1 ? 256 : 64 * WPR; }
+
 // Rows held in registers: VPL values per lane, WPR waves per row (64 * WPR
 // lanes), N <= 64 * WPR * VPL. VEC: each lane moves 16-byte pieces (CH
 // values), piece k of lane t at columns (k * 64 * WPR + t) * CH; otherwise
 // value k of lane t is column k * 64 * WPR + t.
 template <typename TIN, typename TOUT, int WPR, int VPL, bool VEC>
-__global__ __launch_bounds__(kThreads) void softmax_rows(SmParams p) {
-  constexpr int ROWS = 4 / WPR;  // rows per workgroup
+__global__ __launch_bounds__(rows_threads<WPR>()) void softmax_rows(SmParams p) {
+  constexpr int ROWS = rows_threads<WPR>() / (64 * WPR);  // rows per workgroup
   constexpr int T = 64 * WPR;    // lanes per row
   constexpr int CH = 16 / sizeof(TIN);
   constexpr int NP = VEC ? VPL / CH : 0;  // 16-byte pieces per lane
   static_assert(!VEC || NP * CH == VPL, "whole pieces");
-  __shared__ float red[4];
+  __shared__ float red[16];
   const int wave = threadIdx.x >> 6;
   const int sub = wave / WPR;               // row of this workgroup
   const int t = threadIdx.x - sub * T;      // lane within the row
@@ -157,48 +162,82 @@ __global__ __launch_bounds__(kThreads) void softmax_rows(SmParams p) {
 // Long rows: one workgroup per row, two passes. Pass 1 keeps a running
 // maximum and a running sum per thread (rescaled when the maximum grows),
 // pass 2 re-reads the row and writes the normalised values.
-template <typename TIN, typename TOUT>
-__global__ __launch_bounds__(kThreads) void softmax_long(SmParams p) {
-  __shared__ float red[4];
+// One value into the running (maximum, sum) of pass 1, in log2 units.
+__device__ __forceinline__ void online_add(float x, float &m, float &l) {
+  if (x > m) {
+    l = l * __builtin_amdgcn_exp2f(m - x) + 1.f;  // 0 * ... when m was -inf
+    m = x;
+  } else if (x != -INFINITY) {
+    l += __builtin_amdgcn_exp2f(x - m);
+  }
+}
+
+template <typename TIN, typename TOUT, bool VEC>
+__global__ __launch_bounds__(1024) void softmax_long(SmParams p) {
+  constexpr int TH = 1024, CH = 16 / sizeof(TIN), OCH = 16 / sizeof(TOUT);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  __shared__ float red[16];
   const int wave = threadIdx.x >> 6;
   const int64_t row = blockIdx.x;
   const int N = p.N;
   const TIN *xr = static_cast<const TIN *>(p.x) + row * p.xs;
   TOUT *yr = static_cast<TOUT *>(p.y) + row * p.ys;
   float m = -INFINITY, l = 0.f;
-  for (int c = threadIdx.x; c < N; c += kThreads) {
-    const float x = to_f32<TIN>(xr[c]) * kLog2e;
-    if (x > m) {
-      l = l * __builtin_amdgcn_exp2f(m - x) + 1.f;  // 0 * ... when m was -inf
-      m = x;
-    } else if (x != -INFINITY) {
-      l += __builtin_amdgcn_exp2f(x - m);
+  if constexpr (VEC) {
+    for (int c0 = threadIdx.x * CH; c0 < N; c0 += TH * CH) {
+      union { u32x4 w; TIN e[CH]; } u;
+      u.w = *reinterpret_cast<const u32x4 *>(xr + c0);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) online_add(to_f32<TIN>(u.e[e]) * kLog2e, m, l);
     }
+  } else {
+    for (int c = threadIdx.x; c < N; c += TH) online_add(to_f32<TIN>(xr[c]) * kLog2e, m, l);
   }
-  const float mr = row_reduce<4, true>(m, red, wave);
+  const float mr = row_reduce<16, true>(m, red, wave);
   l = l * (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mr));
-  const float inv = 1.0f / row_reduce<4, false>(l, red, wave);
-  for (int c = threadIdx.x; c < N; c += kThreads)
-    yr[c] = from_f32<TOUT>(__builtin_amdgcn_exp2f(fmaf(to_f32<TIN>(xr[c]), kLog2e, -mr)) * inv);
+  const float inv = 1.0f / row_reduce<16, false>(l, red, wave);
+  if constexpr (VEC) {
+    for (int c0 = threadIdx.x * CH; c0 < N; c0 += TH * CH) {
+      union { u32x4 w; TIN e[CH]; } u;
+      u.w = *reinterpret_cast<const u32x4 *>(xr + c0);
+#pragma unroll
+      for (int s = 0; s < CH / OCH; ++s) {
+        union { u32x4 w; TOUT e[OCH]; } o;
+#pragma unroll
+        for (int e = 0; e < OCH; ++e)
+          o.e[e] = from_f32<TOUT>(
+              __builtin_amdgcn_exp2f(fmaf(to_f32<TIN>(u.e[s * OCH + e]), kLog2e, -mr)) * inv);
+        *reinterpret_cast<u32x4 *>(yr + c0 + s * OCH) = o.w;
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < N; c += TH)
+      yr[c] = from_f32<TOUT>(__builtin_amdgcn_exp2f(fmaf(to_f32<TIN>(xr[c]), kLog2e, -mr)) * inv);
+  }
 }
 
 typedef void (*SmFn)(SmParams);
 
+// 64 values per lane at 16 waves fit the 1024-thread register budget only
+// with 16-byte loads; element loads stop at 32 (the host sends longer rows
+// to the two-pass kernel).
 template <typename TIN, typename TOUT, int WPR, bool VEC>
 SmFn pick_vpl(int vpl) {
+  constexpr int VMAX = (WPR == 16 && !VEC) ? 32 : 64;
   switch (vpl) {
     case 8: return softmax_rows<TIN, TOUT, WPR, 8, VEC>;
     case 16: return softmax_rows<TIN, TOUT, WPR, 16, VEC>;
     case 32: return softmax_rows<TIN, TOUT, WPR, 32, VEC>;
-    default: return softmax_rows<TIN, TOUT, WPR, 64, VEC>;
+    default: return softmax_rows<TIN, TOUT, WPR, VMAX, VEC>;
   }
 }
 
 template <typename TIN, typename TOUT>
 SmFn pick_kernel(int wpr, int vpl, bool vec, bool longrow) {
-  if (longrow) return softmax_long<TIN, TOUT>;
+  if (longrow) return vec ? softmax_long<TIN, TOUT, true> : softmax_long<TIN, TOUT, false>;
   if (wpr == 1) return vec ? pick_vpl<TIN, TOUT, 1, true>(vpl) : pick_vpl<TIN, TOUT, 1, false>(vpl);
-  return vec ? pick_vpl<TIN, TOUT, 4, true>(vpl) : pick_vpl<TIN, TOUT, 4, false>(vpl);
+  if (wpr == 4) return vec ? pick_vpl<TIN, TOUT, 4, true>(vpl) : pick_vpl<TIN, TOUT, 4, false>(vpl);
+  return vec ? pick_vpl<TIN, TOUT, 16, true>(vpl) : pick_vpl<TIN, TOUT, 16, false>(vpl);
 }
 
 SmFn pick(attn_dtype in, attn_dtype out, int wpr, int vpl, bool vec, bool longrow) {
@@ -241,6 +280,8 @@ attn_status attn_row_softmax(const void *x, int64_t x_row_stride, void *y, int64
     wpr = 1;
   } else if (N <= 256 * 64) {
     wpr = 4;
+  } else if (N <= 1024 * (vec ? 64 : 32)) {
+    wpr = 16;
   } else {
     longrow = true;
   }
@@ -255,12 +296,13 @@ attn_status attn_row_softmax(const void *x, int64_t x_row_stride, void *y, int64
   p.ys = y_row_stride;
   p.M = (int)M;
   p.N = (int)N;
-  const int64_t rows_per_wg = longrow ? 1 : 4 / wpr;
+  const int64_t rows_per_wg = longrow || wpr > 1 ? 1 : 4;
+  const int threads = longrow ? 1024 : wpr == 1 ? 256 : 64 * wpr;
   const int64_t grid = (M + rows_per_wg - 1) / rows_per_wg;
   SmFn fn = pick(in_dtype, out_dtype, wpr, vpl, vec, longrow);
   void *args[] = {&p};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
-                                         dim3(kThreads), args, 0, (hipStream_t)stream);
+                                         dim3(threads), args, 0, (hipStream_t)stream);
   if (err != hipSuccess) {
     attn_internal::set_last_hip_error((int)err);
     return ATTN_ERR_HIP;

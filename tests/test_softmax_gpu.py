@@ -53,6 +53,10 @@ SHAPES = [
     (7, 1, "bf16", 1.0), (33, 63, "f16", 2.0), (64, 512, "bf16", 1.0),
     (17, 4096, "bf16", 3.0), (9, 4097, "f16", 1.0), (5, 16384, "f32", 1.0),
     (3, 16385, "bf16", 1.0), (2, 70001, "f16", 1.0), (300, 1024, "f16", 1.0),
+    # one 16-wave row per workgroup: 16-byte loads up to 65536, element loads up to 32768
+    (4, 20000, "f16", 1.0), (2, 65536, "bf16", 2.0), (3, 32767, "f32", 1.0),
+    # two passes, 16-byte loads
+    (2, 70000, "bf16", 1.0),
 ]
 
 
