@@ -31,6 +31,10 @@
  * dQ_i needs only row i. dK_j and dV_j need every row that sees key j, so
  * for them the row statistics m_i, l_i and D_i of the whole head are found
  * first (three passes per row, as in the forward's stable softmax).
+ *
+ * A head has Nq query rows and Nk keys; they differ for cross-attention
+ * (which "Triton Kernel Practice" tests its kernel on), where the causal
+ * mask is not defined.
  */
 #include <math.h>
 #include <stdint.h>
@@ -50,8 +54,9 @@ static double dot(const double *a, const double *b, int64_t d) {
   return s;
 }
 
-/* Row statistics of query i of one head: m_i, l_i, and D_i = dO_i . O_i with
- * O_i formed here. `s` and `o_row` are scratch (N and d doubles). */
+/* Row statistics of query i of one head (N keys): m_i, l_i, and
+ * D_i = dO_i . O_i with O_i formed here. `s` and `o_row` are scratch (N and
+ * d doubles). */
 static void row_stats(const double *q, const double *k, const double *v, const double *dout,
                       int64_t N, int64_t d, int causal, double scale, int64_t i, double *s,
                       double *o_row, double *m_out, double *l_out, double *D_out) {
@@ -73,7 +78,7 @@ static void row_stats(const double *q, const double *k, const double *v, const d
   *D_out = dot(dout + i * d, o_row, d);
 }
 
-/* dQ_i of one head. */
+/* dQ_i of one head (N keys). */
 static void dq_row(const double *q, const double *k, const double *v, const double *dout,
                    int64_t N, int64_t d, int causal, double scale, int64_t i, double *s,
                    double *o_row, double *dq) {
@@ -90,7 +95,7 @@ static void dq_row(const double *q, const double *k, const double *v, const doub
   for (int64_t c = 0; c < d; ++c) dq[c] *= scale;
 }
 
-/* dK_j and dV_j of one head from the head's row statistics. */
+/* dK_j and dV_j of one head (N query rows) from the head's row statistics. */
 static void dkdv_row(const double *q, const double *k, const double *v, const double *dout,
                      int64_t N, int64_t d, int causal, double scale, int64_t j,
                      const double *m, const double *l, const double *D, double *dk,
@@ -110,32 +115,36 @@ static void dkdv_row(const double *q, const double *k, const double *v, const do
 }
 
 /*
- * attn_bwd_oracle_rows -- gradients for lists of query and key rows.
+ * attn_bwd_oracle_rows_qk -- gradients for lists of query and key rows, Nq
+ * query rows and Nk keys per head.
  *
- * q, k, v, dout : [B][H][N][d] row-major fp64 (callers upcast the exact
- *                 values the GPU receives).
- * qrows / nq    : flat query row ids (b*H + h)*N + i whose dQ is wanted, or
- *                 NULL with nq = B*H*N for all of them in order.
- * krows / nk    : flat key row ids whose dK and dV are wanted, or NULL with
- *                 nk = B*H*N for all.
- * dq            : [nq][d] out;  dk, dv : [nk][d] out.
- * nthreads      : OpenMP threads (<= 0: the runtime default).
- * Returns ORACLE_OK, ORACLE_BAD_ARG or ORACLE_NO_MEMORY.
+ * q, dout : [B][H][Nq][d] and k, v : [B][H][Nk][d], row-major fp64 (callers
+ *           upcast the exact values the GPU receives).
+ * qrows / nq : flat query row ids (b*H + h)*Nq + i whose dQ is wanted, or
+ *              NULL with nq = B*H*Nq for all of them in order.
+ * krows / nk : flat key row ids (b*H + h)*Nk + j whose dK and dV are wanted,
+ *              or NULL with nk = B*H*Nk for all.
+ * dq : [nq][d] out;  dk, dv : [nk][d] out.
+ * nthreads : OpenMP threads (<= 0: the runtime default).
+ * Returns ORACLE_OK, ORACLE_BAD_ARG (also for a causal mask with Nq != Nk)
+ * or ORACLE_NO_MEMORY.
  */
-int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, const double *dout,
-                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, double scale,
-                         const int64_t *qrows, int64_t nq, double *dq, const int64_t *krows,
-                         int64_t nk, double *dk, double *dv, int nthreads) {
+int attn_bwd_oracle_rows_qk(const double *q, const double *k, const double *v,
+                            const double *dout, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                            int64_t d, int causal, double scale, const int64_t *qrows, int64_t nq,
+                            double *dq, const int64_t *krows, int64_t nk, double *dk, double *dv,
+                            int nthreads) {
   if (!q || !k || !v || !dout) return ORACLE_BAD_ARG;
-  if (B < 1 || H < 1 || N < 1 || d < 1 || nq < 0 || nk < 0) return ORACLE_BAD_ARG;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || d < 1 || nq < 0 || nk < 0) return ORACLE_BAD_ARG;
+  if (causal && Nq != Nk) return ORACLE_BAD_ARG;
   if ((nq > 0 && !dq) || (nk > 0 && (!dk || !dv))) return ORACLE_BAD_ARG;
-  const int64_t BH = B * H, total = BH * N;
-  if ((!qrows && nq != 0 && nq != total) || (!krows && nk != 0 && nk != total))
+  const int64_t BH = B * H, total = BH * Nq, ktotal = BH * Nk;
+  if ((!qrows && nq != 0 && nq != total) || (!krows && nk != 0 && nk != ktotal))
     return ORACLE_BAD_ARG;
   for (int64_t r = 0; qrows && r < nq; ++r)
     if (qrows[r] < 0 || qrows[r] >= total) return ORACLE_BAD_ARG;
   for (int64_t r = 0; krows && r < nk; ++r)
-    if (krows[r] < 0 || krows[r] >= total) return ORACLE_BAD_ARG;
+    if (krows[r] < 0 || krows[r] >= ktotal) return ORACLE_BAD_ARG;
 #ifdef _OPENMP
   if (nthreads <= 0) nthreads = omp_get_max_threads();
 #endif
@@ -146,7 +155,7 @@ int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, cons
 #pragma omp parallel num_threads(nthreads) reduction(| : bad)
 #endif
   {
-    double *s = (double *)malloc((size_t)(N + d) * sizeof(double));
+    double *s = (double *)malloc((size_t)(Nk + d) * sizeof(double));
     if (!s) {
       bad = 1;
     } else {
@@ -155,9 +164,10 @@ int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, cons
 #endif
       for (int64_t r = 0; r < nq; ++r) {
         const int64_t flat = qrows ? qrows[r] : r;
-        const int64_t bh = flat / N, i = flat % N;
-        const size_t head = (size_t)bh * (size_t)N * (size_t)d;
-        dq_row(q + head, k + head, v + head, dout + head, N, d, causal, scale, i, s, s + N,
+        const int64_t bh = flat / Nq, i = flat % Nq;
+        const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;
+        const size_t khead = (size_t)bh * (size_t)Nk * (size_t)d;
+        dq_row(q + qhead, k + khead, v + khead, dout + qhead, Nk, d, causal, scale, i, s, s + Nk,
                dq + r * d);
       }
       free(s);
@@ -175,12 +185,12 @@ int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, cons
     free(need), free(m), free(l), free(D);
     return ORACLE_NO_MEMORY;
   }
-  for (int64_t r = 0; r < nk; ++r) need[(krows ? krows[r] : r) / N] = 1;
+  for (int64_t r = 0; r < nk; ++r) need[(krows ? krows[r] : r) / Nk] = 1;
 #ifdef _OPENMP
 #pragma omp parallel num_threads(nthreads) reduction(| : bad)
 #endif
   {
-    double *s = (double *)malloc((size_t)(N + d) * sizeof(double));
+    double *s = (double *)malloc((size_t)(Nk + d) * sizeof(double));
     if (!s) {
       bad = 1;
     } else {
@@ -188,11 +198,12 @@ int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, cons
 #pragma omp for schedule(dynamic, 8)
 #endif
       for (int64_t flat = 0; flat < total; ++flat) {
-        const int64_t bh = flat / N, i = flat % N;
+        const int64_t bh = flat / Nq, i = flat % Nq;
         if (!need[bh]) continue;
-        const size_t head = (size_t)bh * (size_t)N * (size_t)d;
-        row_stats(q + head, k + head, v + head, dout + head, N, d, causal, scale, i, s, s + N,
-                  m + flat, l + flat, D + flat);
+        const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;
+        const size_t khead = (size_t)bh * (size_t)Nk * (size_t)d;
+        row_stats(q + qhead, k + khead, v + khead, dout + qhead, Nk, d, causal, scale, i, s,
+                  s + Nk, m + flat, l + flat, D + flat);
       }
       free(s);
     }
@@ -203,14 +214,24 @@ int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, cons
 #endif
     for (int64_t r = 0; r < nk; ++r) {
       const int64_t flat = krows ? krows[r] : r;
-      const int64_t bh = flat / N, j = flat % N;
-      const size_t head = (size_t)bh * (size_t)N * (size_t)d;
-      const size_t rows = (size_t)bh * (size_t)N;
-      dkdv_row(q + head, k + head, v + head, dout + head, N, d, causal, scale, j, m + rows,
+      const int64_t bh = flat / Nk, j = flat % Nk;
+      const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;
+      const size_t khead = (size_t)bh * (size_t)Nk * (size_t)d;
+      const size_t rows = (size_t)bh * (size_t)Nq;
+      dkdv_row(q + qhead, k + khead, v + khead, dout + qhead, Nq, d, causal, scale, j, m + rows,
                l + rows, D + rows, dk + r * d, dv + r * d);
     }
   }
   free(need), free(m), free(l), free(D);
   (void)nthreads;
   return bad ? ORACLE_NO_MEMORY : ORACLE_OK;
+}
+
+/* attn_bwd_oracle_rows -- the same with Nq = Nk = N (self-attention). */
+int attn_bwd_oracle_rows(const double *q, const double *k, const double *v, const double *dout,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int causal, double scale,
+                         const int64_t *qrows, int64_t nq, double *dq, const int64_t *krows,
+                         int64_t nk, double *dk, double *dv, int nthreads) {
+  return attn_bwd_oracle_rows_qk(q, k, v, dout, B, H, N, N, d, causal, scale, qrows, nq, dq, krows,
+                                 nk, dk, dv, nthreads);
 }

@@ -72,6 +72,10 @@ def open_bwd_oracle_library(path):
     lib = ctypes.CDLL(path)
     i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
     ip = ctypes.POINTER(i64)
+    lib.attn_bwd_oracle_rows_qk.restype = ctypes.c_int
+    lib.attn_bwd_oracle_rows_qk.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                            ctypes.c_double, ip, i64, dp, ip, i64, dp, dp,
+                                            ctypes.c_int]
     lib.attn_bwd_oracle_rows.restype = ctypes.c_int
     lib.attn_bwd_oracle_rows.argtypes = [dp, dp, dp, dp, i64, i64, i64, i64, ctypes.c_int,
                                          ctypes.c_double, ip, i64, dp, ip, i64, dp, dp,
@@ -162,8 +166,9 @@ def _rows_arg(rows, total):
 
 def attn_bwd_oracle(q, k, v, dout, causal=False, scale=None, qrows=None, krows=None,
                     nthreads=0, lib=None):
-    """fp64 gradients (dQ, dK, dV) of attention of [B,H,N,d] inputs for the
-    upstream gradient dout.
+    """fp64 gradients (dQ, dK, dV) of attention of [B,H,Nq,d] queries over
+    [B,H,Nk,d] keys and values for the upstream gradient dout [B,H,Nq,d]
+    (Nq and Nk may differ when not causal).
 
     scale: the forward's softmax scale; None means 1/sqrt(d).
     qrows: optional flat query row ids (b*H + h)*N + i; dQ is then
@@ -173,28 +178,36 @@ def attn_bwd_oracle(q, k, v, dout, causal=False, scale=None, qrows=None, krows=N
     lib:   another build of attn_bwd_oracle.c (mutant tests).
     """
     q, k, v, dout = _as_f64(q), _as_f64(k), _as_f64(v), _as_f64(dout)
-    if q.ndim != 4 or any(x.shape != q.shape for x in (k, v, dout)):
-        raise ValueError("q, k, v, dout must share one [B,H,N,d] shape")
+    if q.ndim != 4 or k.ndim != 4 or dout.shape != q.shape or v.shape != k.shape or \
+            (k.shape[0], k.shape[1], k.shape[3]) != (q.shape[0], q.shape[1], q.shape[3]):
+        raise ValueError("q, dout [B,H,Nq,d] and k, v [B,H,Nk,d] must agree in B, H and d")
     B, H, N, d = q.shape
+    Nk = k.shape[2]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     lib = lib or _load_bwd()
-    total = B * H * N
-    qa, nq, qp = _rows_arg(qrows, total)
-    ka, nk, kp = _rows_arg(krows, total)
+    qa, nq, qp = _rows_arg(qrows, B * H * N)
+    ka, nk, kp = _rows_arg(krows, B * H * Nk)
     dq = np.empty((nq, d), dtype=np.float64)
     dk = np.empty((nk, d), dtype=np.float64)
     dv = np.empty((nk, d), dtype=np.float64)
     dp = ctypes.POINTER(ctypes.c_double)
-    st = lib.attn_bwd_oracle_rows(q.ctypes.data_as(dp), k.ctypes.data_as(dp),
-                                  v.ctypes.data_as(dp), dout.ctypes.data_as(dp), B, H, N, d,
-                                  int(bool(causal)), float(scale), qp, nq, dq.ctypes.data_as(dp),
-                                  kp, nk, dk.ctypes.data_as(dp), dv.ctypes.data_as(dp),
-                                  int(nthreads))
+    if Nk == N:
+        st = lib.attn_bwd_oracle_rows(q.ctypes.data_as(dp), k.ctypes.data_as(dp),
+                                      v.ctypes.data_as(dp), dout.ctypes.data_as(dp), B, H, N, d,
+                                      int(bool(causal)), float(scale), qp, nq,
+                                      dq.ctypes.data_as(dp), kp, nk, dk.ctypes.data_as(dp),
+                                      dv.ctypes.data_as(dp), int(nthreads))
+    else:
+        st = lib.attn_bwd_oracle_rows_qk(q.ctypes.data_as(dp), k.ctypes.data_as(dp),
+                                         v.ctypes.data_as(dp), dout.ctypes.data_as(dp), B, H, N,
+                                         Nk, d, int(bool(causal)), float(scale), qp, nq,
+                                         dq.ctypes.data_as(dp), kp, nk, dk.ctypes.data_as(dp),
+                                         dv.ctypes.data_as(dp), int(nthreads))
     if st != 0:
         raise RuntimeError("attn_bwd_oracle_rows failed with status %d" % st)
     if qrows is None:
         dq = dq.reshape(B, H, N, d)
     if krows is None:
-        dk, dv = dk.reshape(B, H, N, d), dv.reshape(B, H, N, d)
+        dk, dv = dk.reshape(B, H, Nk, d), dv.reshape(B, H, Nk, d)
     return dq, dk, dv

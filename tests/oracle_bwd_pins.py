@@ -265,9 +265,46 @@ def check_row_subsets(grads):
         _close(sv, dv.reshape(-1, 5)[krows], 0.0, "dV row subset")
 
 
+def check_cross_attention(grads):
+    """Query and key lengths that differ (the shapes "Triton Kernel Practice"
+    validates its forward on, and more): torch's fp64 autograd, every element
+    against central finite differences of the forward oracle on a tiny
+    case, and the Jacobian invariants."""
+    for t, (B, H, nq, nk, d) in enumerate([(1, 1, 5, 15, 32), (1, 1, 1, 10, 64), (2, 3, 7, 19, 8)]):
+        q, dout = _rand((B, H, nq, d), 400 + t), _rand((B, H, nq, d), 410 + t)
+        k, v = _rand((B, H, nk, d), 420 + t), _rand((B, H, nk, d), 430 + t)
+        scale = 1.0 / np.sqrt(d)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        s = (tq @ tk.transpose(-2, -1)) * scale
+        (torch.softmax(s, dim=-1) @ tv).backward(torch.tensor(dout))
+        dq, dk, dv = grads(q, k, v, dout, False, scale)
+        _close(dq, tq.grad.numpy(), 1e-12, "cross dQ %d" % t)
+        _close(dk, tk.grad.numpy(), 1e-12, "cross dK %d" % t)
+        _close(dv, tv.grad.numpy(), 1e-12, "cross dV %d" % t)
+        _close(dk.sum(axis=2), 0.0, 1e-12, "cross dK column sums")
+        _close(dv.sum(axis=2), dout.sum(axis=2), 1e-12, "cross dV column sums")
+    q, dout = _rand((1, 1, 3, 2), 440), _rand((1, 1, 3, 2), 441)
+    k, v = _rand((1, 1, 5, 2), 442), _rand((1, 1, 5, 2), 443)
+    h = 1e-5
+    got = grads(q, k, v, dout, False, 0.8)
+    for which, g in enumerate(got):
+        base = [q, k, v][which]
+        fd = np.zeros(base.shape[2:])
+        for i in range(base.shape[2]):
+            for c in range(base.shape[3]):
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][0, 0, i, c] += h
+                fp = _loss(*args, dout, False, 0.8)
+                args[which][0, 0, i, c] -= 2 * h
+                fm = _loss(*args, dout, False, 0.8)
+                fd[i, c] = (fp - fm) / (2 * h)
+        _close(g[0, 0], fd, 1e-8, "cross finite differences of %s" % "QKV"[which])
+
+
 ALL_CHECKS = [
     check_exercise5_gradient, check_finite_differences, check_torch_autograd,
     check_scale_zero, check_query_zero, check_jacobian_invariants, check_single_key,
     check_causal_edges, check_shift_invariance, check_linearity_in_dout,
     check_key_permutation, check_head_dim_zero_padding, check_large_logits, check_row_subsets,
+    check_cross_attention,
 ]

@@ -39,6 +39,10 @@ MUTANTS = {
     "dq_unnormalised": [("const double p = exp(scale * dot(q + i * d, k + j * d, d) - m) / l;",
                          "const double p = exp(scale * dot(q + i * d, k + j * d, d) - m);")],
     "dkdv_stats_of_wrong_row": [("- m[i]) / l[i];", "- m[j]) / l[j];")],
+    "dkdv_query_head_uses_key_length": [("      const size_t qhead = (size_t)bh * (size_t)Nq * (size_t)d;\n      const size_t khead = (size_t)bh * (size_t)Nk * (size_t)d;\n      const size_t rows",
+                                         "      const size_t qhead = (size_t)bh * (size_t)Nk * (size_t)d;\n      const size_t khead = (size_t)bh * (size_t)Nk * (size_t)d;\n      const size_t rows")],
+    "dq_keys_counted_with_query_length": [("dq_row(q + qhead, k + khead, v + khead, dout + qhead, Nk, d,",
+                                           "dq_row(q + qhead, k + khead, v + khead, dout + qhead, Nk < Nq ? Nk : Nq, d,")],
     "dq_causal_excludes_diagonal": [("  const int64_t n_keys = causal ? i + 1 : N;\n  for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;",
                                      "  const int64_t n_keys = causal ? i : N;\n  for (int64_t c = 0; c < d; ++c) dq[c] = 0.0;")],
 }
