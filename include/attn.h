@@ -177,6 +177,21 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
                      size_t workspace_bytes, void *stream);
 
 /*
+ * attn_bwd_qk -- attn_bwd with Nq query rows and Nk keys per head
+ * (cross-attention). q, o, dout and dq are [B][H][Nq][d]; k, v, dk and dv
+ * are [B][H][Nk][d]; lse is [B][H][Nq]. The workspace holds 8 bytes per
+ * query row: attn_bwd_workspace_bytes(B, H, Nq, d). causal requires
+ * Nq == Nk (else ATTN_ERR_SHAPE). Everything else is as for attn_bwd, which
+ * is this call with Nq = Nk = N.
+ */
+attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void *o,
+                        const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                        attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/*
  * attn_fwd_strided -- the attention forward of attn_fwd for general layouts:
  * Nq query rows against Nk keys per head (cross-attention; the pages'
  * "Triton Kernel Practice" checks its kernel on mismatched query and key

@@ -17,6 +17,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
           4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE"}
 EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_fwd_strided", "attn_bwd",
+           "attn_bwd_qk",
            "attn_bwd_workspace_bytes", "attn_row_softmax", "attn_status_string", "attn_abi_version",
            "attn_last_hip_error")
 
@@ -59,6 +60,10 @@ def load_library(path=LIB_PATH):
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int,
                              ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                              ctypes.c_size_t, vp]
+    lib.attn_bwd_qk.restype = ctypes.c_int
+    lib.attn_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_int, vp, ctypes.c_size_t, vp]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -238,6 +243,16 @@ def attn_bwd_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv
                                    ws_ptr, int(ws_bytes), stream)
 
 
+def attn_bwd_qk_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, Nq,
+                    Nk, d, causal, scale, in_dtype, o_dtype, grad_dtype, ws_ptr, ws_bytes,
+                    stream=None):
+    """Direct call of attn_bwd_qk (Nq query rows, Nk keys); returns the status."""
+    return load_library().attn_bwd_qk(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
+                                      dv_ptr, int(B), int(H), int(Nq), int(Nk), int(d),
+                                      int(bool(causal)), float(scale), int(in_dtype), int(o_dtype),
+                                      int(grad_dtype), ws_ptr, int(ws_bytes), stream)
+
+
 def bwd_workspace_bytes(B, H, N, d):
     """Bytes of device workspace attn_bwd needs (0 for an invalid problem)."""
     return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
@@ -247,13 +262,17 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
              grads=None):
     """Attention backward on the current HIP stream: (dq, dk, dv) for the
     upstream gradient dout, given the forward's inputs, its output o (input
-    dtype or float32) and its lse. grad_dtype defaults to the input dtype
-    (torch.float32 is also accepted). The workspace (a uint8 tensor of at
-    least bwd_workspace_bytes(...) bytes) is taken from torch's allocator when
-    not given. Preallocated (dq, dk, dv) may be passed as `grads`.
+    dtype or float32) and its lse. q, o and dout are [B, H, Nq, d]; k and v
+    [B, H, Nk, d] (Nk may differ from Nq when not causal). grad_dtype
+    defaults to the input dtype (torch.float32 is also accepted). The
+    workspace (a uint8 tensor of at least bwd_workspace_bytes(B, H, Nq, d)
+    bytes) is taken from torch's allocator when not given. Preallocated
+    (dq, dk, dv) may be passed as `grads`.
     """
-    if q.dim() != 4 or any(x.shape != q.shape for x in (k, v, o, dout)):
-        raise ValueError("q, k, v, o, dout must all be [B, H, N, d] of one shape")
+    if q.dim() != 4 or k.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or \
+            v.shape != k.shape or (k.shape[0], k.shape[1], k.shape[3]) != \
+            (q.shape[0], q.shape[1], q.shape[3]):
+        raise ValueError("q, o, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
     if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in (torch.float16,
                                                                             torch.bfloat16):
         raise ValueError("q, k, v, dout must share one dtype, float16 or bfloat16")
@@ -272,21 +291,23 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
     grad_dtype = grad_dtype or q.dtype
     if grad_dtype not in (q.dtype, torch.float32):
         raise ValueError("grad_dtype must be the input dtype or float32")
+    Nk = k.shape[2]
     if grads is None:
-        grads = [torch.empty((B, H, N, d), dtype=grad_dtype, device=q.device) for _ in range(3)]
+        grads = [torch.empty(x.shape, dtype=grad_dtype, device=q.device) for x in (q, k, v)]
     dq, dk, dv = grads
-    if any(g.shape != q.shape or g.dtype != grad_dtype or not g.is_contiguous() or
-           g.device != q.device for g in grads):
-        raise ValueError("grads must be contiguous [B, H, N, d] tensors of grad_dtype on q's device")
+    if any(g.shape != x.shape or g.dtype != grad_dtype or not g.is_contiguous() or
+           g.device != q.device for g, x in zip(grads, (q, k, v))):
+        raise ValueError("grads must be contiguous tensors shaped like q, k, v, of grad_dtype, "
+                         "on q's device")
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                      dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
-                      causal, scale, _TORCH_TO_ATTN[q.dtype], _TORCH_TO_ATTN[o.dtype],
-                      _TORCH_TO_ATTN[grad_dtype], workspace.data_ptr(),
-                      workspace.numel() * workspace.element_size(), stream)
+    st = attn_bwd_qk_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N,
+                         Nk, d, causal, scale, _TORCH_TO_ATTN[q.dtype], _TORCH_TO_ATTN[o.dtype],
+                         _TORCH_TO_ATTN[grad_dtype], workspace.data_ptr(),
+                         workspace.numel() * workspace.element_size(), stream)
     if st != 0:
         msg = status_string(st)
         if st == 5:

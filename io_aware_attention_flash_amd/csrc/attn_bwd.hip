@@ -64,7 +64,7 @@ struct BwdParams {
   const float *lse;
   void *dq, *dk, *dv;
   f32x2 *ld;  // workspace: (L * log2 e, D) per query row
-  int N;
+  int Nq, Nk;  // query rows and keys per head (equal when causal)
   int BH;
   float qk;     // scale * log2(e)
   float scale;  // applied to dQ and dK
@@ -311,43 +311,43 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   const int l32 = lane & 31, g = lane >> 5;
   const int kbk = blockIdx.x / p.BH;  // small k0 first: causal blocks with most work start first
   const int bh = blockIdx.x - kbk * p.BH;
-  const int N = p.N;
+  const int Nq = p.Nq, Nk = p.Nk;
   const int k0 = kbk * kBlockK, kw0 = k0 + 32 * wave;
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head;
-  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head;
-  const f32x2 *LDh = p.ld + (size_t)bh * N;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + qhead;
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + khead;
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + khead;
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + qhead;
+  const f32x2 *LDh = p.ld + (size_t)bh * Nq;
 
   uint16_t *vlds = lds;
   auto stage = [&](int s) { return lds + S::V_ELEMS + s * S::STAGE; };
 
   const uint32_t qvoff = QCopy::src_offset(tid);
   const int q_begin = CAUSAL ? k0 : 0;
-  const int n_qt = (N - q_begin + kTileQ - 1) / kTileQ;
+  const int n_qt = (Nq - q_begin + kTileQ - 1) / kTileQ;
 
   // Copies of query tile `it` into stage it & 1: Q and dO by every wave, LD by wave 0.
   auto issue = [&](int it) {
     const int q0 = q_begin + it * kTileQ;
     uint16_t *st = stage(it & 1);
-    QCopy::issue(Qh, q0, N, st, qvoff, wave);
-    QCopy::issue(dOh, q0, N, st + S::TILE, qvoff, wave);
+    QCopy::issue(Qh, q0, Nq, st, qvoff, wave);
+    QCopy::issue(dOh, q0, Nq, st + S::TILE, qvoff, wave);
     if (wave == 0) {
-      const int rows = min(N - q0, kTileQ);
+      const int rows = min(Nq - q0, kTileQ);
       const u32x4 rs = make_rsrc(LDh + q0, (uint32_t)rows * 8);
       dma16(rs, __builtin_amdgcn_readfirstlane(lds_addr(st + 2 * S::TILE)), lane * 16);
     }
   };
 
   // V block (this workgroup's 128 keys) into LDS, and the first query tile.
-  VCopy::issue(Vh, k0, N, vlds, VCopy::src_offset(tid), wave);
+  VCopy::issue(Vh, k0, Nk, vlds, VCopy::src_offset(tid), wave);
   issue(0);
 
   // K operand of S = Q K^T for this wave's keys: K[kw0 + l32][16kc + 8g ..].
   u32x4 kf[NKC];
   {
-    const bool ok = kw0 + l32 < N;
+    const bool ok = kw0 + l32 < Nk;
     const uint16_t *kr = Kh + (size_t)(ok ? kw0 + l32 : 0) * D + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
       // P = exp2(S * qk - L2), with masked pairs (key after query, key or
       // query past the end) set to 0; dS = P (dP - D). Both packed as the
       // operands of the two accumulating products.
-      const bool edge = (CAUSAL && q0 < kw0 + 32) || kw0 + 32 > N || q0 + kTileQ > N;
+      const bool edge = (CAUSAL && q0 < kw0 + 32) || kw0 + 32 > Nk || q0 + kTileQ > Nq;
       uint32_t pp[8], dsp[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
           float x = __builtin_amdgcn_exp2f(s[4 * j + r] * qk - l2[r]);
           if (edge) {
             const int qrow = q0 + 8 * j + 4 * g + r;
-            const bool keep = (!CAUSAL || my_key <= qrow) && my_key < N && qrow < N;
+            const bool keep = (!CAUSAL || my_key <= qrow) && my_key < Nk && qrow < Nq;
             x = keep ? x : 0.f;
           }
           pr[r] = x;
@@ -426,8 +426,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   }
 
   // dV^T / dK^T accumulators: lane holds key my_key, columns 32cb + 8j + 4g + 0..3.
-  if (my_key < N) {
-    const size_t row = (size_t)bh * N + my_key;
+  if (my_key < Nk) {
+    const size_t row = (size_t)bh * Nk + my_key;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -469,34 +469,34 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int N = p.N;
-  const int nqb = (N + kBlockQ - 1) / kBlockQ;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int nqb = (Nq + kBlockQ - 1) / kBlockQ;
   const int t_ = blockIdx.x / p.BH;
   const int bh = blockIdx.x - t_ * p.BH;
   const int qb = CAUSAL ? nqb - 1 - t_ : t_;  // causal: longest first
   const int m0 = qb * kBlockQ, qw0 = m0 + 32 * wave;
   const int my_q = qw0 + l32;
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head;
-  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head;
+  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + qhead;
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + khead;
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + khead;
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + qhead;
 
   const uint32_t kvoff = KCopy::src_offset(tid);
-  const int kend = CAUSAL ? min(N, m0 + kBlockQ) : N;
+  const int kend = CAUSAL ? min(Nk, m0 + kBlockQ) : Nk;
   const int n_kt = (kend + kTileK - 1) / kTileK;
   auto stage = [&](int s) { return lds + s * S::STAGE; };
   auto issue = [&](int it) {
     uint16_t *st = stage(it & 1);
-    KCopy::issue(Kh, it * kTileK, N, st, kvoff, wave);
-    KCopy::issue(Vh, it * kTileK, N, st + S::TILE, kvoff, wave);
+    KCopy::issue(Kh, it * kTileK, Nk, st, kvoff, wave);
+    KCopy::issue(Vh, it * kTileK, Nk, st + S::TILE, kvoff, wave);
   };
   issue(0);
 
   // Q and dO operands of S^T = K Q^T and dP^T = V dO^T: row my_q, 16kc + 8g ..
   u32x4 qf[NKC], df[NKC];
   {
-    const bool ok = my_q < N;
+    const bool ok = my_q < Nq;
     const size_t r = (size_t)(ok ? my_q : 0) * D + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -504,7 +504,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       df[kc] = ok ? *reinterpret_cast<const u32x4 *>(dOh + r + 16 * kc) : u32x4{0, 0, 0, 0};
     }
   }
-  const f32x2 ldv = my_q < N ? p.ld[(size_t)bh * N + my_q] : f32x2{0.f, 0.f};
+  const f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
   const float l2 = ldv[0], dd = ldv[1];
   const TrAddr<D> ta = tr_addr<D>(lane);
   f32x16 dqt[NCB];
@@ -532,13 +532,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       for (int kc = 0; kc < NKC; ++kc) s = mfma<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) dp = mfma<IS_BF16>(row_frag<D>(vt, 32 * kb + l32, 2 * kc + g), df[kc], dp);
-      const bool edge = (CAUSAL && key0 + 31 > qw0) || key0 + 32 > N;
+      const bool edge = (CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float x = __builtin_amdgcn_exp2f(s[e] * qk - l2);
         if (edge) {
           const int key = key0 + 8 * (e >> 2) + 4 * g + (e & 3);
-          const bool keep = (!CAUSAL || key <= my_q) && key < N;
+          const bool keep = (!CAUSAL || key <= my_q) && key < Nk;
           x = keep ? x : 0.f;
         }
         dp[e] = x * (dp[e] - dd);  // dS
@@ -556,8 +556,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
   }
 
   // dQ^T accumulators: lane holds query my_q, columns 32cb + 8j + 4g + 0..3.
-  if (my_q < N) {
-    const size_t row = (size_t)bh * N + my_q;
+  if (my_q < Nq) {
+    const size_t row = (size_t)bh * Nq + my_q;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -616,25 +616,28 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   return ws_bytes(B, H, N);
 }
 
-attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
-                     const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
-                     int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
-                     attn_dtype o_dtype, attn_dtype grad_dtype, void *workspace,
-                     size_t workspace_bytes, void *stream) {
+attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void *o,
+                        const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                        attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream) {
   // Validation first: no HIP call happens before every argument is checked.
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return ATTN_ERR_SHAPE;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+  if (Nq > (int64_t(1) << 24) || Nk > (int64_t(1) << 24) || B * H > (int64_t(1) << 24))
+    return ATTN_ERR_SHAPE;
+  if (causal && Nq != Nk) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   if (o_dtype != in_dtype && o_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  const size_t need = ws_bytes(B, H, N);
+  const size_t need = ws_bytes(B, H, Nq);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return ATTN_ERR_WORKSPACE;
-  const int64_t nkb = (N + kBlockK - 1) / kBlockK, nqb = (N + kBlockQ - 1) / kBlockQ;
-  const int64_t rows = B * H * N;
+  const int64_t nkb = (Nk + kBlockK - 1) / kBlockK, nqb = (Nq + kBlockQ - 1) / kBlockQ;
+  const int64_t rows = B * H * Nq;
   const int64_t lpr = d / 8;
   const int64_t prep_blocks = (rows * lpr + 255) / 256;
   if (nkb * B * H > INT32_MAX || nqb * B * H > INT32_MAX || prep_blocks > INT32_MAX)
@@ -651,7 +654,8 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
   p.dk = dk;
   p.dv = dv;
   p.ld = reinterpret_cast<f32x2 *>(workspace);
-  p.N = (int)N;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
   p.BH = (int)(B * H);
   p.qk = (float)((double)scale * 1.4426950408889634);
   p.scale = scale;
@@ -686,6 +690,15 @@ attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o,
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+                     const void *dout, void *dq, void *dk, void *dv, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
+                     attn_dtype o_dtype, attn_dtype grad_dtype, void *workspace,
+                     size_t workspace_bytes, void *stream) {
+  return attn_bwd_qk(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, N, d, causal, scale, in_dtype,
+                     o_dtype, grad_dtype, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

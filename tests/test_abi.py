@@ -211,3 +211,15 @@ def test_row_softmax_error_paths_need_no_gpu(lib, args, code):
     st = binding.row_softmax_raw(a["x"] or None, a["xs"], a["y"] or None, a["ys"], a["M"], a["N"],
                                  a["i"], a["o"])
     assert st == code, (args, st)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(Nk=0), 2), (dict(Nq=0), 2), (dict(causal=1), 2),   # causal needs Nq == Nk
+    (dict(d=96), 3), (dict(ws=0), 6),
+])
+def test_bwd_qk_error_paths_need_no_gpu(lib, args, code):
+    a = dict(B=1, H=1, Nq=64, Nk=80, d=64, causal=0, ws=P)
+    a.update(args)
+    st = binding.attn_bwd_qk_raw(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["Nq"], a["Nk"],
+                                 a["d"], a["causal"], 0.125, 2, 0, 0, a["ws"] or None, 1 << 20)
+    assert st == code, (args, st)

@@ -249,6 +249,31 @@ def test_bwd_deterministic():
         assert torch.equal(x, y)
 
 
+CROSS = [
+    # (B, H, Nq, Nk, d, dtype, sigma): query and key lengths that differ
+    (1, 1, 1, 10, 64, "f16", 1.0), (1, 1, 5, 15, 64, "bf16", 1.0),
+    (2, 3, 300, 77, 128, "bf16", 1.0), (1, 2, 64, 1000, 64, "f16", 1.0),
+    (1, 1, 129, 257, 128, "bf16", 3.0), (1, 2, 700, 33, 128, "f16", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", CROSS, ids=lambda c: "B%dH%dNq%dNk%dd%d_%s_s%g" % c)
+def test_bwd_cross_attention(case):
+    """attn_bwd_qk with Nq != Nk; O and LSE from the oracle (fp32)."""
+    B, H, Nq, Nk, d, dt, sigma = case
+    _say("case", case)
+    q = make_qkv(B, H, Nq, d, dt, sigma, seed=15)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dt, sigma, seed=16)
+    dout = make_dout(B, H, Nq, d, dt, seed=15)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, False, scale)
+    got = gpu_bwd(q, k, v, o, lse, dout, False, scale)
+    assert got[0].shape == q.shape and got[1].shape == k.shape and got[2].shape == v.shape
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=False, scale=scale)
+    terms, extra = _terms(q, k, v, dout, False, scale)
+    check_grads(got, ref, terms, extra, U[dt], "cross %s" % (case,))
+
+
 # ------------------------------------------------ full-size, sampled rows
 
 FULL = ["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16"]

@@ -54,6 +54,30 @@ def test_autograd_matches_oracles(B, H, N, d, dt, causal):
     check_grads(got, ref, terms, extra, U[dt], "autograd", grad_rounding=U[dt])
 
 
+def test_autograd_cross_attention():
+    """Queries and keys of different lengths through the operator: the
+    forward takes the general-layout kernel, the backward attn_bwd_qk."""
+    B, H, Nq, Nk, d, dt = 2, 2, 150, 333, 128, "bf16"
+    q = make_qkv(B, H, Nq, d, dt, 1.0, seed=23)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dt, 1.0, seed=24)
+    dout = make_dout(B, H, Nq, d, dt, seed=23)
+    scale = float(torch.tensor(1.0 / d ** 0.5, dtype=torch.float32))
+    dev = torch.device("cuda:0")
+    qg, kg, vg = (x.to(dev).requires_grad_() for x in (q, k, v))
+    o = flash_attn_func(qg, kg, vg, causal=False, scale=scale)
+    o.backward(dout.to(dev))
+    torch.cuda.synchronize()
+    ro, _ = oracle.attn_oracle(q, k, v, causal=False, scale=scale)
+    ulp = np.abs(ro) * U[dt] + 1e-30
+    assert np.all(np.abs(o.detach().cpu().double().numpy() - ro) <= 1e-2 + 0.5 * ulp + 2 ** -24)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=False, scale=scale)
+    dD = (dout.double().abs() * (1e-2 + 0.5 * torch.from_numpy(ulp))).sum(-1)
+    dL = torch.full((B, H, Nq), 1e-3, dtype=torch.float64)
+    terms, extra = _terms(q, k, v, dout, False, scale, dD=dD, dL=dL)
+    got = [x.grad.float().cpu() for x in (qg, kg, vg)]
+    check_grads(got, ref, terms, extra, U[dt], "autograd cross", grad_rounding=U[dt])
+
+
 def test_opcheck():
     """torch's operator checks: schema, fake tensors, autograd registration."""
     q, k, v = (x.cuda() for x in make_qkv(1, 2, 64, 64, "bf16", 1.0, seed=22))
