@@ -56,7 +56,11 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kBlockK = 128;   // keys per dK/dV workgroup (32 per wave)
 constexpr int kTileQ = 32;     // queries per dK/dV step
 constexpr int kBlockQ = 128;   // queries per dQ workgroup (32 per wave)
-constexpr int kTileK = 64;     // keys per dQ step
+#ifndef ATTN_CFG_BWD_DQ_TILE_K  // keys per dQ step; -D overrides it for a sweep
+#define ATTN_CFG_BWD_DQ_TILE_K 64
+#endif
+constexpr int kTileK = ATTN_CFG_BWD_DQ_TILE_K;
+static_assert(kTileK == 32 || kTileK == 64 || kTileK == 128, "dQ key tile");
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {

@@ -168,12 +168,30 @@ struct Shape16 {
   static_assert(DMA_INS * INS_BYTES == TILE_BYTES, "each DMA instruction moves 16 bytes a thread");
 };
 
+// Compile-time configuration. The defaults are the measured choices; a build
+// may override them with -D (io_aware_attention_flash_amd/sweep.py builds
+// and times the alternatives).
+#ifndef ATTN_CFG_RESCALE_LOG2
+#define ATTN_CFG_RESCALE_LOG2 8
+#endif
+#ifndef ATTN_CFG_LOOKAHEAD
+#define ATTN_CFG_LOOKAHEAD 3
+#endif
+#ifndef ATTN_CFG_PREPASS_MIN_N
+#define ATTN_CFG_PREPASS_MIN_N 8192
+#endif
+
 // Rows of the online softmax are rescaled only when their maximum grows by
 // more than this many powers of two; otherwise exponentials are taken
-// against the stale maximum and stay <= 2^8, which fp16 P and the fp32
-// accumulators hold exactly as well. The final O / l and LSE use the same
-// reference, so the result is the same in exact arithmetic.
-constexpr float kRescaleLog2 = 8.0f;
+// against the stale maximum and stay <= 2^8 (at the default), which fp16 P
+// and the fp32 accumulators hold exactly as well. The final O / l and LSE
+// use the same reference, so the result is the same in exact arithmetic.
+constexpr float kRescaleLog2 = ATTN_CFG_RESCALE_LOG2;
+static_assert(ATTN_CFG_RESCALE_LOG2 >= 0 && ATTN_CFG_RESCALE_LOG2 <= 15, "fp16 P holds up to 2^15");
+
+// LDS operand reads run this many MFMA steps ahead of their use.
+constexpr int kLookahead = ATTN_CFG_LOOKAHEAD;
+static_assert(kLookahead >= 1 && kLookahead <= 6, "lookahead range");
 
 // Chunk swizzles: chunk x of row r is stored at x ^ swz(r).
 //  K: the 16 rows one K operand read touches (same logical chunk) land on 16
@@ -325,12 +343,12 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t *vst, const LaneAddr<D> &
 }
 
 // S^T[kb] = K_kb Q^T for one tile (once per query tile, before the
-// pipelined loop), the K operands read three steps ahead of their MFMAs.
+// pipelined loop), the K operands read kLookahead steps ahead of their MFMAs.
 template <int D, bool IS_BF16>
 __device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *kst,
                                         const LaneAddr<D> &la) {
   using S = Shape16<D>;
-  constexpr int NM = S::NKB * S::NKC, LA = 3;
+  constexpr int NM = S::NKB * S::NKC, LA = kLookahead;
   u32x4 fr[LA + 1];
 #pragma unroll
   for (int i = 0; i < LA; ++i) fr[i] = k_frag<D>(kst, la, i / S::NKC, i % S::NKC);
@@ -480,9 +498,6 @@ struct Pipe16 {
     for (int c = 0; c < Shape16<D>::DMA_INS; ++c) *v_slot(t, c) = to_f16(*v_slot(t, c));
   }
 };
-
-// LDS operand reads run this many MFMA steps ahead of their use.
-constexpr int kLookahead = 3;
 
 // Step at which score pair p (P^T dword p % 4 of PV operand p / 4, scores
 // of block p / 8) takes its exponent argument; its exponential follows one
@@ -1056,7 +1071,7 @@ constexpr int kPrepassBlocks = 8192;
 // The first pass costs about as much as the in-LDS conversion saves at
 // N = 4096 (causal) and pays off from about twice that: kernel time grows
 // with N^2, the pass with N.
-constexpr int64_t kPrepassMinN = 8192;
+constexpr int64_t kPrepassMinN = ATTN_CFG_PREPASS_MIN_N;
 
 // --------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.

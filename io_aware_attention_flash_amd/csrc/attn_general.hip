@@ -48,7 +48,20 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kBlockM = 128;   // queries per workgroup (32 per wave)
-constexpr int kTileK = 64;     // keys per step (bf16 / fp16)
+// Keys per step (bf16 / fp16), per head dimension: the sweep of this choice
+// (io_aware_attention_flash_amd/sweep.py) measured 32 fastest at d = 128 and
+// 64 at d = 64. -D ATTN_CFG_GEN_TILE_K overrides both.
+template <int D>
+constexpr int gen_tile_k() {
+#ifdef ATTN_CFG_GEN_TILE_K
+  return ATTN_CFG_GEN_TILE_K;
+#else
+  return D == 128 ? 32 : 64;
+#endif
+}
+static_assert(gen_tile_k<64>() % 32 == 0 && gen_tile_k<64>() <= 128 && gen_tile_k<128>() % 32 == 0 &&
+                  gen_tile_k<128>() <= 128, "key tile");
+constexpr int kTileKMax = 128;  // the largest key tile any build uses
 constexpr float kRescaleLog2 = 8.0f;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a source offset past any range
 
@@ -203,7 +216,8 @@ struct GenCopy {
 
 template <int D>
 struct GenShape {
-  static constexpr int TILE = kTileK * D;
+  static constexpr int TK = gen_tile_k<D>();
+  static constexpr int TILE = TK * D;
   static constexpr int STAGE = 2 * TILE;  // K, V
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
@@ -211,6 +225,7 @@ struct GenShape {
 template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
   using S = GenShape<D>;
+  constexpr int kTileK = S::TK;
   using Copy = GenCopy<D, kTileK>;
   constexpr int NKC = D / 16, NCB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
@@ -554,8 +569,8 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
       !view_ok(v, p.vs, B, H, Nk, d, eb) || !view_ok(o, p.os, B, H, Nq, d, ob))
     return ATTN_ERR_UNSUPPORTED;
   // a 64-key tile of K or V must fit the 32-bit range of a buffer descriptor
-  if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileK >= (int64_t(1) << 31) ||
-                               p.vs[2] * eb * kTileK >= (int64_t(1) << 31)))
+  if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileKMax >= (int64_t(1) << 31) ||
+                               p.vs[2] * eb * kTileKMax >= (int64_t(1) << 31)))
     return ATTN_ERR_UNSUPPORTED;
   const int64_t nq = (Nq + kBlockM - 1) / kBlockM;
   const int64_t grid = nq * B * H;

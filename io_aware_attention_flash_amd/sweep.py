@@ -1,0 +1,246 @@
+"""Offline sweep of the kernels' compile-time configurations: the gfx950
+counterpart of the pages' autotuning ("4.4 Writing GPU Kernels with Triton",
+sections "Sizing the attention kernel" and "Autotuning": time a list of
+tile configurations per problem size and keep the best).
+
+Triton compiles a configuration when it is first called. Here the tile
+shapes are compile-time constants of hand-written kernels, so the
+alternatives are built ahead of time: each knob below is a -D macro whose
+default is the configuration the library ships. `build` compiles one library
+per alternative (on any host: hipcc cross-compiles for gfx950); `run` times
+the alternatives against the default on the GPU, interleaved in one process,
+and compares their outputs with the default's.
+
+    python -m io_aware_attention_flash_amd.sweep build
+    python -m io_aware_attention_flash_amd.sweep run [--write PATH]
+
+Libraries go to build/sweep/ at the repository root; results to
+build/sweep/results.json, and with --write to a markdown table.
+"""
+import argparse
+import concurrent.futures
+import ctypes
+import json
+import os
+import subprocess
+import sys
+import time
+
+from . import build as hipbuild
+
+SWEEP_DIR = os.path.join(hipbuild.ROOT, "build", "sweep")
+
+# knob -> the macro, its values (the first is what the library ships: a number,
+# or a label when the shipped value depends on the head dimension), the pass
+# that exercises it and the workloads it is timed on.
+KNOBS = {
+    "fwd_lookahead": dict(macro="ATTN_CFG_LOOKAHEAD", values=[3, 2, 4], pass_="fwd",
+                          workloads=["b2h32_n4096_d128_bf16_causal",
+                                     "b1h16_n16384_d128_bf16_sigma3_causal"],
+                          what="LDS operand reads issued this many MFMA steps ahead"),
+    "fwd_rescale_log2": dict(macro="ATTN_CFG_RESCALE_LOG2", values=[8, 0, 4], pass_="fwd",
+                             workloads=["b2h32_n4096_d128_bf16_causal",
+                                        "b1h16_n16384_d128_bf16_sigma3_causal"],
+                             what="lazy rescale: rescale only when the row maximum grows by "
+                                  "more than 2^value (0: whenever it grows)"),
+    "fwd_prepass_min_n": dict(macro="ATTN_CFG_PREPASS_MIN_N", values=[8192, 4096, 1 << 30],
+                              pass_="fwd_ws",
+                              workloads=["b2h32_n4096_d128_bf16_causal",
+                                         "b1h32_n8192_d128_bf16_causal",
+                                         "b1h16_n16384_d128_bf16_sigma3_causal"],
+                              what="bf16 V converted to fp16 by a first pass from this N on "
+                                   "(2^30: never)"),
+    "bwd_dq_tile_k": dict(macro="ATTN_CFG_BWD_DQ_TILE_K", values=[64, 32, 128], pass_="bwd",
+                          workloads=["b2h32_n4096_d128_bf16_causal",
+                                     "b8h12_n3000_d64_f16"],
+                          what="keys per step of the backward's dQ kernel"),
+    "gen_tile_k": dict(macro="ATTN_CFG_GEN_TILE_K", values=["32@d128/64@d64", 32, 64, 128],
+                       pass_="general",
+                       workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                       what="keys per step of the general-layout forward"),
+}
+
+
+def variant_name(knob, value):
+    return "default" if value == KNOBS[knob]["values"][0] else "%s_%d" % (knob, value)
+
+
+def _alternatives(knob):
+    """The values of a knob other than the shipped one (each a -D build)."""
+    return KNOBS[knob]["values"][1:]
+
+
+def lib_path(name):
+    return os.path.join(SWEEP_DIR, "lib_%s.so" % name)
+
+
+def _build_one(name, defs):
+    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
+    out = lib_path(name)
+    cmd = [hipcc] + hipbuild.HIPCC_FLAGS + defs + ["-I", hipbuild.INCLUDE] + hipbuild.SRCS + \
+        ["-o", out]
+    t0 = time.time()
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr[-4000:])
+        raise RuntimeError("hipcc failed for %s" % name)
+    bad = hipbuild.scratch_users(res.stderr)
+    if bad:
+        os.remove(out)
+        raise RuntimeError("%s: kernels use scratch memory: %s" % (name, bad))
+    return "built %-28s %s (%.0f s)" % (name, " ".join(defs) or "(shipped)", time.time() - t0)
+
+
+def build_all(jobs=4):
+    os.makedirs(SWEEP_DIR, exist_ok=True)
+    todo = [("default", [])]
+    for knob, k in KNOBS.items():
+        for v in _alternatives(knob):
+            todo.append((variant_name(knob, v), ["-D%s=%d" % (k["macro"], v)]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for msg in ex.map(lambda t: _build_one(*t), todo):
+            print(msg, flush=True)
+
+
+def _workload(name):
+    from .inputs import WORKLOADS, Workload
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    if name == "b1h32_n8192_d128_bf16_causal":
+        return Workload(name, 1, 32, 8192, 128, "bf16", True)
+    raise KeyError(name)
+
+
+def _runner(lib, w, pass_, tensors):
+    """A zero-argument function that enqueues one call of `pass_` through
+    the library `lib` on the prepared tensors."""
+    import torch
+    from . import binding
+    q, k, v, o, lse, dout, grads, ws, qs = tensors
+    dt = {"bf16": binding.ATTN_BF16, "f16": binding.ATTN_F16}[w.dtype]
+    stream = torch.cuda.current_stream().cuda_stream
+    if pass_ == "fwd":
+        return lambda: lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), w.B, w.H, w.N, w.d, int(w.causal), w.scale, dt,
+                                    binding.ATTN_F32, stream)
+    if pass_ == "fwd_ws":
+        need = lib.attn_fwd_workspace_bytes(w.B, w.H, w.N, w.d, dt)
+        ptr = ws.data_ptr() if need else None
+        return lambda: lib.attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), w.B, w.H, w.N, w.d, int(w.causal), w.scale,
+                                       dt, binding.ATTN_F32, ptr, ws.numel(), stream)
+    if pass_ == "bwd":
+        nws = lib.attn_bwd_workspace_bytes(w.B, w.H, w.N, w.d)
+        return lambda: lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), dout.data_ptr(), grads[0].data_ptr(),
+                                    grads[1].data_ptr(), grads[2].data_ptr(), w.B, w.H, w.N, w.d,
+                                    int(w.causal), w.scale, dt, binding.ATTN_F32,
+                                    binding.ATTN_F32, ws.data_ptr(), nws, stream)
+    if pass_ == "general":
+        sq = (ctypes.c_int64 * 3)(*qs[0].stride()[:3])
+        return lambda: lib.attn_fwd_strided(qs[0].data_ptr(), sq, qs[1].data_ptr(), sq,
+                                            qs[2].data_ptr(), sq, o.data_ptr(), None,
+                                            lse.data_ptr(), w.B, w.H, w.N, w.N, w.d,
+                                            int(w.causal), w.scale, dt, binding.ATTN_F32, stream)
+    raise ValueError(pass_)
+
+
+def run_all(rounds=8, target_ms=60.0):
+    import torch
+    from . import binding
+    from .inputs import make_dout, workload_qkv
+    results = []
+    for knob, kn in KNOBS.items():
+        names = [variant_name(knob, v) for v in kn["values"]]
+        libs = {n: binding.load_library(lib_path(n)) for n in names}
+        for wl in kn["workloads"]:
+            w = _workload(wl)
+            dev = torch.device("cuda:0")
+            q, k, v = (x.to(dev) for x in workload_qkv(w, seed=0))
+            dout = make_dout(w.B, w.H, w.N, w.d, w.dtype, seed=0).to(dev)
+            o = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+            nws = max(w.B * w.H * w.N * w.d * 2, w.B * w.H * w.N * 8) + 256
+            ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+            qs = [x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v)]
+            if kn["pass_"] == "bwd":  # the backward's O and LSE, from the shipped forward
+                assert libs[names[0]].attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                               o.data_ptr(), lse.data_ptr(), w.B, w.H, w.N, w.d,
+                                               int(w.causal), w.scale,
+                                               {"bf16": 2, "f16": 1}[w.dtype], 0,
+                                               torch.cuda.current_stream().cuda_stream) == 0
+            tensors = (q, k, v, o, lse, dout, grads, ws, qs)
+            calls = {n: _runner(libs[n], w, kn["pass_"], tensors) for n in names}
+            out = grads if kn["pass_"] == "bwd" else [o, lse]
+
+            def timed(n, count):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(count):
+                    calls[n]()
+                e1.record()
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) / count
+
+            ms1 = timed(names[0], 3)
+            per = max(3, int(target_ms / max(ms1, 1e-3)))
+            for n in names:  # warm every variant, then time them in alternating order
+                timed(n, per)
+            times = {n: [] for n in names}
+            for r in range(rounds):
+                for n in (names if r % 2 == 0 else names[::-1]):
+                    times[n].append(timed(n, per))
+            ref = None
+            base = sorted(times[names[0]])[rounds // 2]
+            for n in names:
+                for x in out:
+                    x.zero_()
+                assert calls[n]() == 0
+                torch.cuda.synchronize()
+                got = [x.clone() for x in out]
+                if ref is None:
+                    ref = got
+                diff = max(float((a - b).abs().max()) for a, b in zip(got, ref))
+                med = sorted(times[n])[len(times[n]) // 2]
+                results.append(dict(knob=knob, macro=kn["macro"], value=kn["values"][names.index(n)],
+                                    shipped=n == names[0], workload=wl, pass_=kn["pass_"],
+                                    us=med * 1e3, rel=base / med - 1.0,
+                                    max_abs_diff_vs_shipped=diff))
+                print("%-18s %-10s %-40s %9.1f us  %+6.2f%%  diff %.1e" % (
+                    knob, results[-1]["value"], wl, med * 1e3, 100 * results[-1]["rel"], diff),
+                    flush=True)
+    with open(os.path.join(SWEEP_DIR, "results.json"), "w") as f:
+        json.dump(results, f, indent=1)
+    return results
+
+
+def markdown(results):
+    lines = ["| knob (macro) | value | pass | workload | µs | vs shipped | max abs diff vs shipped |",
+             "|---|---|---|---|---|---|---|"]
+    for r in results:
+        lines.append("| %s (`%s`) | %s%s | %s | %s | %.1f | %+.2f%% | %.1e |" % (
+            r["knob"], r["macro"], r["value"], " (shipped)" if r["shipped"] else "", r["pass_"],
+            r["workload"], r["us"], 100 * r["rel"], r["max_abs_diff_vs_shipped"]))
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("what", choices=["build", "run"])
+    ap.add_argument("--write", help="markdown file for the results table (run)")
+    ap.add_argument("--jobs", type=int, default=4, help="parallel compilations (build)")
+    args = ap.parse_args(argv)
+    if args.what == "build":
+        build_all(args.jobs)
+        return
+    res = run_all()
+    table = markdown(res)
+    print(table)
+    if args.write:
+        with open(args.write, "w") as f:
+            f.write(table + "\n")
+
+
+if __name__ == "__main__":
+    main()
