@@ -311,7 +311,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   constexpr int NKC = D / 16, NCB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is read through a scalar register so that everything derived
+  // from it (this wave's keys, the edge test below) is known to be wave-uniform
+  // and branches on it are scalar branches, not per-lane masks.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int kbk = blockIdx.x / p.BH;  // small k0 first: causal blocks with most work start first
   const int bh = blockIdx.x - kbk * p.BH;
@@ -390,29 +394,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
       // P = exp2(S * qk - L2), with masked pairs (key after query, key or
       // query past the end) set to 0; dS = P (dP - D). Both packed as the
       // operands of the two accumulating products.
-      const bool edge = (CAUSAL && q0 < kw0 + 32) || kw0 + 32 > Nk || q0 + kTileQ > Nq;
-      uint32_t pp[8], dsp[8];
+      // P in place of S and dP - D in place of dP.
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 a = ldt[4 * j + 2 * g], b = ldt[4 * j + 2 * g + 1];  // rows 8j+4g .. +3
         const float l2[4] = {a[0], a[2], b[0], b[2]};
         const float dd[4] = {a[1], a[3], b[1], b[3]};
-        float pr[4], dr[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float x = __builtin_amdgcn_exp2f(s[4 * j + r] * qk - l2[r]);
-          if (edge) {
-            const int qrow = q0 + 8 * j + 4 * g + r;
-            const bool keep = (!CAUSAL || my_key <= qrow) && my_key < Nk && qrow < Nq;
-            x = keep ? x : 0.f;
-          }
-          pr[r] = x;
-          dr[r] = x * (dp[4 * j + r] - dd[r]);
+          s[4 * j + r] = __builtin_amdgcn_exp2f(s[4 * j + r] * qk - l2[r]);
+          dp[4 * j + r] -= dd[r];
         }
-        pp[2 * j] = pack2<IS_BF16>(pr[0], pr[1]);
-        pp[2 * j + 1] = pack2<IS_BF16>(pr[2], pr[3]);
-        dsp[2 * j] = pack2<IS_BF16>(dr[0], dr[1]);
-        dsp[2 * j + 1] = pack2<IS_BF16>(dr[2], dr[3]);
+      }
+      // Only tiles on the diagonal or past an end hold masked pairs; the test
+      // is wave-uniform, so interior tiles skip the masking entirely.
+      if ((CAUSAL && q0 < kw0 + 32) || kw0 + 32 > Nk || q0 + kTileQ > Nq) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qrow = q0 + 8 * (e >> 2) + 4 * g + (e & 3);
+          const bool keep = (!CAUSAL || my_key <= qrow) && my_key < Nk && qrow < Nq;
+          s[e] = keep ? s[e] : 0.f;
+        }
+      }
+      uint32_t pp[8], dsp[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        pp[j] = pack2<IS_BF16>(s[2 * j], s[2 * j + 1]);
+        dsp[j] = pack2<IS_BF16>(s[2 * j] * dp[2 * j], s[2 * j + 1] * dp[2 * j + 1]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (operand t: elements 8t .. 8t+7)
 #pragma unroll
@@ -471,7 +479,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
   constexpr int NKC = D / 16, NCB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Wave index through a scalar register: see bwd_dkdv.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nqb = (Nq + kBlockQ - 1) / kBlockQ;
@@ -536,17 +546,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       for (int kc = 0; kc < NKC; ++kc) s = mfma<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) dp = mfma<IS_BF16>(row_frag<D>(vt, 32 * kb + l32, 2 * kc + g), df[kc], dp);
-      const bool edge = (CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float x = __builtin_amdgcn_exp2f(s[e] * qk - l2);
-        if (edge) {
+      for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(s[e] * qk - l2);  // P
+      // Masked pairs only on the diagonal or past the last key (wave-uniform test).
+      if ((CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
           const int key = key0 + 8 * (e >> 2) + 4 * g + (e & 3);
           const bool keep = (!CAUSAL || key <= my_q) && key < Nk;
-          x = keep ? x : 0.f;
+          s[e] = keep ? s[e] : 0.f;
         }
-        dp[e] = x * (dp[e] - dd);  // dS
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dp[e] = s[e] * (dp[e] - dd);  // dS
       // dQ^T += K^T dS^T
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
