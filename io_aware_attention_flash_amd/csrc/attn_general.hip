@@ -287,6 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
   for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
   float m = -INFINITY, l = 0.f;
   const float qk = p.qk;
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
 #pragma unroll 1
   for (int it = 0; it < n_kt; ++it) {
@@ -309,17 +310,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
         s = mfma_in<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
-      const bool edge = (CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk;
-      float mx = -INFINITY;
+      // Masked pairs only on the diagonal or past the last key: one
+      // wave-uniform branch around all 16 selects.
+      if ((CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (edge) {
+        for (int e = 0; e < 16; ++e) {
           const int key = key0 + 8 * (e >> 2) + 4 * g + (e & 3);
           const bool keep = (!CAUSAL || key <= qrow) && key < Nk;
           s[e] = keep ? s[e] : -INFINITY;
         }
-        mx = fmaxf(mx, s[e]);
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * qk;  // both key halves of this query
       // Lazy rescale: the state moves to a new maximum only when it grew by
       // more than 2^8 (every p stays <= 256, which fp16 holds exactly enough);
@@ -342,9 +345,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
         const float p0 = __builtin_amdgcn_exp2f(s[e] * qk - mref);
         const float p1 = __builtin_amdgcn_exp2f(s[e + 1] * qk - mref);
         pp[e >> 1] = pack_f16(p0, p1);
-        // the row sum takes the rounded weights, as the products do
-        const f16x2 hp = __builtin_bit_cast(f16x2, pp[e >> 1]);
-        l += (float)hp[0] + (float)hp[1];
+        // the row sum takes the rounded weights, as the products do: one
+        // fp16 pair dot (1, 1) accumulated in fp32
+        l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp[e >> 1]), ones, l, false);
       }
       // O^T += V^T P^T
 #pragma unroll
