@@ -384,17 +384,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
     if (!CAUSAL || q0 + kTileQ - 1 >= kw0) {
       // S = Q K^T and dP = dO V^T: lane (key my_key) holds queries
       // q0 + 8j + 4g + r in element 4j + r of each.
+      // Steps i < NKC: S += Q_kc K_kc^T (K from registers); the other NKC
+      // steps: dP += dO_kc V_kc^T. Each step's LDS operands are read one step
+      // ahead, so an MFMA does not wait on the read just issued for it.
       f32x16 s = f32x16{}, dp = f32x16{};
+      auto opa = [&](int i) {
+        return i < NKC ? row_frag<D>(qt, l32, 2 * i + g) : row_frag<D>(dot, l32, 2 * (i - NKC) + g);
+      };
+      auto opb = [&](int i) {
+        return i < NKC ? kf[i] : row_frag<D>(vlds, 32 * wave + l32, 2 * (i - NKC) + g);
+      };
+      {
+        u32x4 a0 = opa(0), b0 = opb(0);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) {
-        s = mfma<IS_BF16>(row_frag<D>(qt, l32, 2 * kc + g), kf[kc], s);
-        dp = mfma<IS_BF16>(row_frag<D>(dot, l32, 2 * kc + g),
-                           row_frag<D>(vlds, 32 * wave + l32, 2 * kc + g), dp);
+        for (int i = 0; i < 2 * NKC; ++i) {
+          u32x4 a1 = a0, b1 = b0;
+          if (i + 1 < 2 * NKC) {
+            a1 = opa(i + 1);
+            b1 = opb(i + 1);
+          }
+          __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMA
+          if (i < NKC) s = mfma<IS_BF16>(a0, b0, s); else dp = mfma<IS_BF16>(a0, b0, dp);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
+          b0 = b1;
+        }
       }
-      // P = exp2(S * qk - L2), with masked pairs (key after query, key or
-      // query past the end) set to 0; dS = P (dP - D). Both packed as the
-      // operands of the two accumulating products.
-      // P in place of S and dP - D in place of dP.
+      // P = exp2(S * qk - L2) in place of S and dP - D in place of dP; masked
+      // pairs (key after query, key or query past the end) get P = 0. Then
+      // P and dS = P (dP - D) are packed as the operands of dV and dK.
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const f32x4 a = ldt[4 * j + 2 * g], b = ldt[4 * j + 2 * g + 1];  // rows 8j+4g .. +3
@@ -423,14 +441,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
         dsp[j] = pack2<IS_BF16>(s[2 * j] * dp[2 * j], s[2 * j + 1] * dp[2 * j + 1]);
       }
       // dV^T += dO^T P and dK^T += Q^T dS (operand t: elements 8t .. 8t+7)
+      // Step i: operand t = i / (2 NCB), column block cb = (i / 2) % NCB, dV
+      // for even i and dK for odd i; the transposing reads one step ahead.
+      {
+        auto opt = [&](int i) {
+          return tr_frag<D>((i & 1) ? qt : dot, ta, i / (2 * NCB), (i >> 1) % NCB);
+        };
+        u32x4 a0 = opt(0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
-        const u32x4 df = {dsp[4 * t], dsp[4 * t + 1], dsp[4 * t + 2], dsp[4 * t + 3]};
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          dvt[cb] = mfma<IS_BF16>(tr_frag<D>(dot, ta, t, cb), pf, dvt[cb]);
-          dkt[cb] = mfma<IS_BF16>(tr_frag<D>(qt, ta, t, cb), df, dkt[cb]);
+        for (int i = 0; i < 4 * NCB; ++i) {
+          u32x4 a1 = a0;
+          if (i + 1 < 4 * NCB) a1 = opt(i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          const int t = i / (2 * NCB), cb = (i >> 1) % NCB;
+          if (i & 1) {
+            const u32x4 df = {dsp[4 * t], dsp[4 * t + 1], dsp[4 * t + 2], dsp[4 * t + 3]};
+            dkt[cb] = mfma<IS_BF16>(a0, df, dkt[cb]);
+          } else {
+            const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
+            dvt[cb] = mfma<IS_BF16>(a0, pf, dvt[cb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
         }
       }
     }
@@ -541,11 +573,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       const int key0 = it * kTileK + 32 * kb;
       if (CAUSAL && key0 > qw0 + 31) continue;  // every key after every query of this wave
       // S^T = K Q^T: lane (query my_q) holds keys key0 + 8j + 4g + r in s[4j + r].
+      // Steps i < NKC: S^T += K_kc Q_kc^T; the other NKC: dP^T += V_kc dO_kc^T
+      // (Q and dO from registers). The LDS operand is read one step ahead.
       f32x16 s = f32x16{}, dp = f32x16{};
+      {
+        auto opa = [&](int i) {
+          return row_frag<D>(i < NKC ? kt : vt, 32 * kb + l32, 2 * (i % NKC) + g);
+        };
+        u32x4 a0 = opa(0);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) s = mfma<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) dp = mfma<IS_BF16>(row_frag<D>(vt, 32 * kb + l32, 2 * kc + g), df[kc], dp);
+        for (int i = 0; i < 2 * NKC; ++i) {
+          u32x4 a1 = a0;
+          if (i + 1 < 2 * NKC) a1 = opa(i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i < NKC) s = mfma<IS_BF16>(a0, qf[i], s); else dp = mfma<IS_BF16>(a0, df[i - NKC], dp);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
+        }
+      }
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(s[e] * qk - l2);  // P
       // Masked pairs only on the diagonal or past the last key (wave-uniform test).
@@ -560,12 +605,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) dp[e] = s[e] * (dp[e] - dd);  // dS
       // dQ^T += K^T dS^T
+      {
+        const uint16_t *kk = kt + 32 * kb * D;
+        const u32x4 sf[2] = {acc_frag<IS_BF16>(dp, 0), acc_frag<IS_BF16>(dp, 1)};
+        u32x4 a0 = tr_frag<D>(kk, ta, 0, 0);
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 sf = acc_frag<IS_BF16>(dp, t);
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          dqt[cb] = mfma<IS_BF16>(tr_frag<D>(kt + 32 * kb * D, ta, t, cb), sf, dqt[cb]);
+        for (int i = 0; i < 2 * NCB; ++i) {  // t = i / NCB, cb = i % NCB
+          u32x4 a1 = a0;
+          if (i + 1 < 2 * NCB) a1 = tr_frag<D>(kk, ta, (i + 1) / NCB, (i + 1) % NCB);
+          __builtin_amdgcn_sched_barrier(0);
+          dqt[i % NCB] = mfma<IS_BF16>(a0, sf[i / NCB], dqt[i % NCB]);
+          __builtin_amdgcn_sched_barrier(0);
+          a0 = a1;
+        }
       }
     }
     lds_barrier();
