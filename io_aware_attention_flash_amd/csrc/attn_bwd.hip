@@ -61,6 +61,11 @@ constexpr int kBlockQ = 128;   // queries per dQ workgroup (32 per wave)
 #endif
 constexpr int kTileK = ATTN_CFG_BWD_DQ_TILE_K;
 static_assert(kTileK == 32 || kTileK == 64 || kTileK == 128, "dQ key tile");
+#ifndef ATTN_CFG_BWD_LOOKAHEAD  // MFMA steps by which LDS operand reads run ahead
+#define ATTN_CFG_BWD_LOOKAHEAD 2
+#endif
+constexpr int kBwdLookahead = ATTN_CFG_BWD_LOOKAHEAD;
+static_assert(kBwdLookahead >= 1 && kBwdLookahead <= 3, "lookahead range");
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
@@ -136,6 +141,29 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const TrAddr<D> &
   const u32x2 w0 = __builtin_bit_cast(u32x2, r0), w1 = __builtin_bit_cast(u32x2, r1);
   return u32x4{w0[0], w0[1], w1[0], w1[1]};
 }
+
+// Runs MFMA steps 0 .. N-1: step i's LDS operands, op(i), are read kBwdLookahead
+// steps before run(i, operands) issues its MFMA. Scheduling barriers keep the
+// reads ahead of the MFMAs; the compiler waits only for the reads a step uses.
+template <int N, class Op, class Run>
+__device__ __forceinline__ void pipelined(Op op, Run run) {
+  constexpr int LA = kBwdLookahead < N ? kBwdLookahead : N;
+  using T = decltype(op(0));
+  T fr[LA + 1];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) fr[i] = op(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + LA < N) fr[(i + LA) % (LA + 1)] = op(i + LA);
+    __builtin_amdgcn_sched_barrier(0);
+    run(i, fr[i % (LA + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+struct FragPair {
+  u32x4 a, b;
+};
 
 // fp32 pair -> packed bf16 / fp16, round to nearest even.
 template <bool IS_BF16>
@@ -385,31 +413,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
       // S = Q K^T and dP = dO V^T: lane (key my_key) holds queries
       // q0 + 8j + 4g + r in element 4j + r of each.
       // Steps i < NKC: S += Q_kc K_kc^T (K from registers); the other NKC
-      // steps: dP += dO_kc V_kc^T. Each step's LDS operands are read one step
-      // ahead, so an MFMA does not wait on the read just issued for it.
+      // steps: dP += dO_kc V_kc^T. LDS operands are read ahead (pipelined).
       f32x16 s = f32x16{}, dp = f32x16{};
-      auto opa = [&](int i) {
-        return i < NKC ? row_frag<D>(qt, l32, 2 * i + g) : row_frag<D>(dot, l32, 2 * (i - NKC) + g);
-      };
-      auto opb = [&](int i) {
-        return i < NKC ? kf[i] : row_frag<D>(vlds, 32 * wave + l32, 2 * (i - NKC) + g);
-      };
-      {
-        u32x4 a0 = opa(0), b0 = opb(0);
-#pragma unroll
-        for (int i = 0; i < 2 * NKC; ++i) {
-          u32x4 a1 = a0, b1 = b0;
-          if (i + 1 < 2 * NKC) {
-            a1 = opa(i + 1);
-            b1 = opb(i + 1);
-          }
-          __builtin_amdgcn_sched_barrier(0);  // the reads go out before the MFMA
-          if (i < NKC) s = mfma<IS_BF16>(a0, b0, s); else dp = mfma<IS_BF16>(a0, b0, dp);
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = a1;
-          b0 = b1;
-        }
-      }
+      pipelined<2 * NKC>(
+          [&](int i) {
+            return i < NKC ? FragPair{row_frag<D>(qt, l32, 2 * i + g), kf[i]}
+                           : FragPair{row_frag<D>(dot, l32, 2 * (i - NKC) + g),
+                                      row_frag<D>(vlds, 32 * wave + l32, 2 * (i - NKC) + g)};
+          },
+          [&](int i, const FragPair &f) {
+            if (i < NKC) s = mfma<IS_BF16>(f.a, f.b, s); else dp = mfma<IS_BF16>(f.a, f.b, dp);
+          });
       // P = exp2(S * qk - L2) in place of S and dP - D in place of dP; masked
       // pairs (key after query, key or query past the end) get P = 0. Then
       // P and dS = P (dP - D) are packed as the operands of dV and dK.
@@ -442,29 +456,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
       }
       // dV^T += dO^T P and dK^T += Q^T dS (operand t: elements 8t .. 8t+7)
       // Step i: operand t = i / (2 NCB), column block cb = (i / 2) % NCB, dV
-      // for even i and dK for odd i; the transposing reads one step ahead.
-      {
-        auto opt = [&](int i) {
-          return tr_frag<D>((i & 1) ? qt : dot, ta, i / (2 * NCB), (i >> 1) % NCB);
-        };
-        u32x4 a0 = opt(0);
-#pragma unroll
-        for (int i = 0; i < 4 * NCB; ++i) {
-          u32x4 a1 = a0;
-          if (i + 1 < 4 * NCB) a1 = opt(i + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          const int t = i / (2 * NCB), cb = (i >> 1) % NCB;
-          if (i & 1) {
-            const u32x4 df = {dsp[4 * t], dsp[4 * t + 1], dsp[4 * t + 2], dsp[4 * t + 3]};
-            dkt[cb] = mfma<IS_BF16>(a0, df, dkt[cb]);
-          } else {
-            const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
-            dvt[cb] = mfma<IS_BF16>(a0, pf, dvt[cb]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = a1;
-        }
-      }
+      // for even i and dK for odd i; the transposing reads run ahead.
+      pipelined<4 * NCB>(
+          [&](int i) { return tr_frag<D>((i & 1) ? qt : dot, ta, i / (2 * NCB), (i >> 1) % NCB); },
+          [&](int i, const u32x4 &a) {
+            const int t = i / (2 * NCB), cb = (i >> 1) % NCB;
+            if (i & 1) {
+              const u32x4 df = {dsp[4 * t], dsp[4 * t + 1], dsp[4 * t + 2], dsp[4 * t + 3]};
+              dkt[cb] = mfma<IS_BF16>(a, df, dkt[cb]);
+            } else {
+              const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
+              dvt[cb] = mfma<IS_BF16>(a, pf, dvt[cb]);
+            }
+          });
     }
     lds_barrier();  // stage it & 1 is refilled by the next iteration's copies
   }
@@ -574,23 +578,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       if (CAUSAL && key0 > qw0 + 31) continue;  // every key after every query of this wave
       // S^T = K Q^T: lane (query my_q) holds keys key0 + 8j + 4g + r in s[4j + r].
       // Steps i < NKC: S^T += K_kc Q_kc^T; the other NKC: dP^T += V_kc dO_kc^T
-      // (Q and dO from registers). The LDS operand is read one step ahead.
+      // (Q and dO from registers). The LDS operand is read ahead.
       f32x16 s = f32x16{}, dp = f32x16{};
-      {
-        auto opa = [&](int i) {
-          return row_frag<D>(i < NKC ? kt : vt, 32 * kb + l32, 2 * (i % NKC) + g);
-        };
-        u32x4 a0 = opa(0);
-#pragma unroll
-        for (int i = 0; i < 2 * NKC; ++i) {
-          u32x4 a1 = a0;
-          if (i + 1 < 2 * NKC) a1 = opa(i + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          if (i < NKC) s = mfma<IS_BF16>(a0, qf[i], s); else dp = mfma<IS_BF16>(a0, df[i - NKC], dp);
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = a1;
-        }
-      }
+      pipelined<2 * NKC>(
+          [&](int i) { return row_frag<D>(i < NKC ? kt : vt, 32 * kb + l32, 2 * (i % NKC) + g); },
+          [&](int i, const u32x4 &a) {
+            if (i < NKC) s = mfma<IS_BF16>(a, qf[i], s); else dp = mfma<IS_BF16>(a, df[i - NKC], dp);
+          });
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(s[e] * qk - l2);  // P
       // Masked pairs only on the diagonal or past the last key (wave-uniform test).
@@ -608,16 +602,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       {
         const uint16_t *kk = kt + 32 * kb * D;
         const u32x4 sf[2] = {acc_frag<IS_BF16>(dp, 0), acc_frag<IS_BF16>(dp, 1)};
-        u32x4 a0 = tr_frag<D>(kk, ta, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2 * NCB; ++i) {  // t = i / NCB, cb = i % NCB
-          u32x4 a1 = a0;
-          if (i + 1 < 2 * NCB) a1 = tr_frag<D>(kk, ta, (i + 1) / NCB, (i + 1) % NCB);
-          __builtin_amdgcn_sched_barrier(0);
-          dqt[i % NCB] = mfma<IS_BF16>(a0, sf[i / NCB], dqt[i % NCB]);
-          __builtin_amdgcn_sched_barrier(0);
-          a0 = a1;
-        }
+        pipelined<2 * NCB>(  // step i: t = i / NCB, cb = i % NCB
+            [&](int i) { return tr_frag<D>(kk, ta, i / NCB, i % NCB); },
+            [&](int i, const u32x4 &a) { dqt[i % NCB] = mfma<IS_BF16>(a, sf[i / NCB], dqt[i % NCB]); });
       }
     }
     lds_barrier();

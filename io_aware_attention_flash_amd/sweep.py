@@ -54,6 +54,10 @@ KNOBS = {
                           workloads=["b2h32_n4096_d128_bf16_causal",
                                      "b8h12_n3000_d64_f16"],
                           what="keys per step of the backward's dQ kernel"),
+    "bwd_lookahead": dict(macro="ATTN_CFG_BWD_LOOKAHEAD", values=[2, 1], pass_="bwd",
+                          workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                          what="MFMA steps by which the backward's LDS operand reads run ahead "
+                               "(3 spills)"),
     "gen_tile_k": dict(macro="ATTN_CFG_GEN_TILE_K", values=["32@d128/64@d64", 32, 64, 128],
                        pass_="general",
                        workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
