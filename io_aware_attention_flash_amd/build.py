@@ -2,7 +2,8 @@
 
 The library holds the forward (csrc/attn_fwd.hip), the backward
 (csrc/attn_bwd.hip), the general-layout forward (csrc/attn_general.hip) and
-the row softmax (csrc/softmax.hip).
+the row softmax (csrc/softmax.hip); csrc/mfma_pipe.h is shared by the
+backward and the general forward.
 
     python -m io_aware_attention_flash_amd.build
 
@@ -71,7 +72,7 @@ def is_stale():
     if not os.path.exists(LIB):
         return True
     t = os.path.getmtime(LIB)
-    srcs = SRCS + [os.path.join(INCLUDE, "attn.h")]
+    srcs = SRCS + [os.path.join(INCLUDE, "attn.h"), os.path.join(PKG, "csrc", "mfma_pipe.h")]
     return any(os.path.getmtime(s) > t for s in srcs)
 
 

@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include "attn.h"
+#include "mfma_pipe.h"
 
 namespace attn_internal {
 void set_last_hip_error(int e);
@@ -142,23 +143,9 @@ __device__ __forceinline__ u32x4 tr_frag(const uint16_t *tile, const TrAddr<D> &
   return u32x4{w0[0], w0[1], w1[0], w1[1]};
 }
 
-// Runs MFMA steps 0 .. N-1: step i's LDS operands, op(i), are read kBwdLookahead
-// steps before run(i, operands) issues its MFMA. Scheduling barriers keep the
-// reads ahead of the MFMAs; the compiler waits only for the reads a step uses.
 template <int N, class Op, class Run>
 __device__ __forceinline__ void pipelined(Op op, Run run) {
-  constexpr int LA = kBwdLookahead < N ? kBwdLookahead : N;
-  using T = decltype(op(0));
-  T fr[LA + 1];
-#pragma unroll
-  for (int i = 0; i < LA; ++i) fr[i] = op(i);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (i + LA < N) fr[(i + LA) % (LA + 1)] = op(i + LA);
-    __builtin_amdgcn_sched_barrier(0);
-    run(i, fr[i % (LA + 1)]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  mfma_pipelined<N, kBwdLookahead>(op, run);
 }
 
 struct FragPair {

@@ -30,6 +30,7 @@
 #include <stdint.h>
 
 #include "attn.h"
+#include "mfma_pipe.h"
 
 namespace attn_internal {
 void set_last_hip_error(int e);
@@ -62,6 +63,11 @@ constexpr int gen_tile_k() {
 static_assert(gen_tile_k<64>() % 32 == 0 && gen_tile_k<64>() <= 128 && gen_tile_k<128>() % 32 == 0 &&
                   gen_tile_k<128>() <= 128, "key tile");
 constexpr int kTileKMax = 128;  // the largest key tile any build uses
+#ifndef ATTN_CFG_GEN_LOOKAHEAD  // MFMA steps by which LDS operand reads run ahead
+#define ATTN_CFG_GEN_LOOKAHEAD 2
+#endif
+constexpr int kGenLookahead = ATTN_CFG_GEN_LOOKAHEAD;
+static_assert(kGenLookahead >= 1 && kGenLookahead <= 4, "lookahead range");
 constexpr float kRescaleLog2 = 8.0f;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a source offset past any range
 
@@ -307,9 +313,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
       if (key0 >= Nk) continue;
       // S^T: lane (query qrow) holds keys key0 + 8j + 4g + r in s[4j + r].
       f32x16 s = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-        s = mfma_in<IS_BF16>(row_frag<D>(kt, 32 * kb + l32, 2 * kc + g), qf[kc], s);
+      mfma_pipelined<NKC, kGenLookahead>(
+          [&](int kc) { return row_frag<D>(kt, 32 * kb + l32, 2 * kc + g); },
+          [&](int kc, const u32x4 &a) { s = mfma_in<IS_BF16>(a, qf[kc], s); });
       // Masked pairs only on the diagonal or past the last key: one
       // wave-uniform branch around all 16 selects.
       if ((CAUSAL && key0 + 31 > qw0) || key0 + 32 > Nk) {
@@ -350,13 +356,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
         l = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp[e >> 1]), ones, l, false);
       }
       // O^T += V^T P^T
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-          acc[cb] = mfma_f16(tr_frag<D>(vt + 32 * kb * D, ta, t, cb), pf, acc[cb]);
-      }
+      mfma_pipelined<2 * NCB, kGenLookahead>(  // step i: t = i / NCB, cb = i % NCB
+          [&](int i) { return tr_frag<D>(vt + 32 * kb * D, ta, i / NCB, i % NCB); },
+          [&](int i, const u32x4 &a) {
+            const int t = i / NCB;
+            const u32x4 pf = {pp[4 * t], pp[4 * t + 1], pp[4 * t + 2], pp[4 * t + 3]};
+            acc[i % NCB] = mfma_f16(a, pf, acc[i % NCB]);
+          });
     }
     lds_barrier();
   }

@@ -1,0 +1,23 @@
+// Software pipelining of LDS operand reads ahead of the MFMAs that use them.
+#pragma once
+
+// Runs MFMA steps 0 .. N-1: step i's LDS operands, op(i), are read LA steps
+// before run(i, operands) issues its MFMA. Scheduling barriers keep each
+// step's reads ahead of its MFMA (without them the scheduler sinks a read to
+// just before its use); the compiler then waits only for the reads a step
+// uses, while the next LA steps' reads are in flight.
+template <int N, int LA_, class Op, class Run>
+__device__ __forceinline__ void mfma_pipelined(Op op, Run run) {
+  constexpr int LA = LA_ < N ? LA_ : N;
+  using T = decltype(op(0));
+  T fr[LA + 1];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) fr[i] = op(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (i + LA < N) fr[(i + LA) % (LA + 1)] = op(i + LA);
+    __builtin_amdgcn_sched_barrier(0);
+    run(i, fr[i % (LA + 1)]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}

@@ -58,6 +58,10 @@ KNOBS = {
                           workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
                           what="MFMA steps by which the backward's LDS operand reads run ahead "
                                "(3 spills)"),
+    "gen_lookahead": dict(macro="ATTN_CFG_GEN_LOOKAHEAD", values=[2, 1, 3], pass_="general",
+                          workloads=["b2h32_n4096_d128_bf16_causal", "b4h16_n1024_d64_bf16"],
+                          what="MFMA steps by which the general kernel's LDS operand reads run "
+                               "ahead"),
     "gen_tile_k": dict(macro="ATTN_CFG_GEN_TILE_K", values=["32@d128/64@d64", 32, 64, 128],
                        pass_="general",
                        workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
