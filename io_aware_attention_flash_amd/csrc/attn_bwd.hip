@@ -216,6 +216,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Makes `x` (loaded from global memory before a loop) complete here. The
+// compiler's wait for such a load otherwise lands at its first use inside
+// the loop, as a vmcnt(0) that each iteration would also spend waiting for
+// that iteration's tile copies.
+template <class T>
+__device__ __forceinline__ void settle(T &x) {
+  asm volatile("" : "+v"(x));
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -375,6 +384,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
       kf[kc] = ok ? *reinterpret_cast<const u32x4 *>(kr + 16 * kc) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) settle(kf[kc]);
   }
   const TrAddr<D> ta = tr_addr<D>(lane);
   f32x16 dvt[NCB], dkt[NCB];
@@ -541,7 +552,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       df[kc] = ok ? *reinterpret_cast<const u32x4 *>(dOh + r + 16 * kc) : u32x4{0, 0, 0, 0};
     }
   }
-  const f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
+  f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    settle(qf[kc]);
+    settle(df[kc]);
+  }
+  settle(ldv);
   const float l2 = ldv[0], dd = ldv[1];
   const TrAddr<D> ta = tr_addr<D>(lane);
   f32x16 dqt[NCB];
