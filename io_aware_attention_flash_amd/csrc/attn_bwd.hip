@@ -216,15 +216,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Makes `x` (loaded from global memory before a loop) complete here. The
-// compiler's wait for such a load otherwise lands at its first use inside
-// the loop, as a vmcnt(0) that each iteration would also spend waiting for
-// that iteration's tile copies.
-template <class T>
-__device__ __forceinline__ void settle(T &x) {
-  asm volatile("" : "+v"(x));
-}
-
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();

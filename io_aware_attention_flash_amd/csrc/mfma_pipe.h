@@ -1,5 +1,17 @@
-// Software pipelining of LDS operand reads ahead of the MFMAs that use them.
+// Software pipelining around the MFMAs: LDS operand reads run ahead of the
+// MFMAs that use them, and register operands loaded before a loop are made
+// complete before it.
 #pragma once
+
+// Makes `x` (loaded from global memory before a loop) complete here. The
+// compiler's wait for such a load otherwise lands at its first use inside
+// the loop, as a vmcnt(0) that each iteration would also spend waiting for
+// that iteration's tile copies (issued by inline assembly the compiler does
+// not count).
+template <class T>
+__device__ __forceinline__ void settle(T &x) {
+  asm volatile("" : "+v"(x));
+}
 
 // Runs MFMA steps 0 .. N-1: step i's LDS operands, op(i), are read LA steps
 // before run(i, operands) issues its MFMA. Scheduling barriers keep each
