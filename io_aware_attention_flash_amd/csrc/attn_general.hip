@@ -577,7 +577,7 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
   if (!view_ok(q, p.qs, B, H, Nq, d, eb) || !view_ok(k, p.ks, B, H, Nk, d, eb) ||
       !view_ok(v, p.vs, B, H, Nk, d, eb) || !view_ok(o, p.os, B, H, Nq, d, ob))
     return ATTN_ERR_UNSUPPORTED;
-  // a 64-key tile of K or V must fit the 32-bit range of a buffer descriptor
+  // a key tile (up to kTileKMax rows) of K or V must fit the 32-bit range of a buffer descriptor
   if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileKMax >= (int64_t(1) << 31) ||
                                p.vs[2] * eb * kTileKMax >= (int64_t(1) << 31)))
     return ATTN_ERR_UNSUPPORTED;

@@ -148,6 +148,36 @@ def test_parity_workload_sampled(name, seed):
         assert bool((lse.double() >= diag - 1e-3).all())
 
 
+# ------------------------------------------------------------ long sequences
+LONG_CASES = [
+    # (B, H, N, d, dtype, causal): one head at a million keys (row and key
+    # indices past 2^19, 4096 query tiles), and a non-causal fp16 d=64 head
+    # at 2^18
+    (1, 1, 1 << 20, 128, "bf16", True),
+    (1, 1, 1 << 18, 64, "f16", False),
+]
+
+
+@pytest.mark.parametrize("case", LONG_CASES, ids=lambda c: "N%d_d%d_%s_%s" % (
+    c[2], c[3], c[4], "causal" if c[5] else "full"))
+def test_long_sequence_sampled(case):
+    """Sampled rows of one very long head against the oracle: the first and
+    last rows, rows on both sides of query-tile and pairing boundaries, and
+    random rows."""
+    B, H, N, d, dt, causal = case
+    _say("long sequence", case)
+    q, k, v = make_qkv(B, H, N, d, dt, 1.0, seed=5)
+    sc = _scale(d)
+    o, lse = gpu_attn(q, k, v, causal, sc)
+    rng = np.random.default_rng(5)
+    fixed = [0, 1, 127, 128, 255, 256, 257, N // 2 - 1, N // 2, N - 257, N - 256, N - 129, N - 1]
+    rows = np.array(sorted(set(fixed + list(rng.integers(0, N, 8)))), dtype=np.int64)
+    ref_o, ref_l = oracle.attn_oracle(q, k, v, causal=causal, scale=sc, rows=rows)
+    check_close(o.reshape(-1, d).numpy()[rows], lse.reshape(-1).numpy()[rows], ref_o, ref_l,
+                "N=%d d=%d (%d sampled rows)" % (N, d, len(rows)))
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
 # ------------------------------------------------------------- special cases
 def test_exercise5_embedded():
     """Exercise 5 of the Triton chapter inside a d=64 head: q0 = e0,
