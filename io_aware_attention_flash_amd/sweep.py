@@ -11,8 +11,8 @@ per alternative (on any host: hipcc cross-compiles for gfx950); `run` times
 the alternatives against the default on the GPU, interleaved in one process,
 and compares their outputs with the default's.
 
-    python -m io_aware_attention_flash_amd.sweep build
-    python -m io_aware_attention_flash_amd.sweep run [--write PATH]
+    python -m io_aware_attention_flash_amd.sweep build [--knobs K ...]
+    python -m io_aware_attention_flash_amd.sweep run [--knobs K ...] [--write PATH]
 
 Libraries go to build/sweep/ at the repository root; results to
 build/sweep/results.json, and with --write to a markdown table.
@@ -99,10 +99,12 @@ def _build_one(name, defs):
     return "built %-28s %s (%.0f s)" % (name, " ".join(defs) or "(shipped)", time.time() - t0)
 
 
-def build_all(jobs=4):
+def build_all(jobs=4, knobs=None):
     os.makedirs(SWEEP_DIR, exist_ok=True)
     todo = [("default", [])]
     for knob, k in KNOBS.items():
+        if knobs and knob not in knobs:
+            continue
         for v in _alternatives(knob):
             todo.append((variant_name(knob, v), ["-D%s=%d" % (k["macro"], v)]))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -153,12 +155,14 @@ def _runner(lib, w, pass_, tensors):
     raise ValueError(pass_)
 
 
-def run_all(rounds=8, target_ms=60.0):
+def run_all(rounds=8, target_ms=60.0, knobs=None):
     import torch
     from . import binding
     from .inputs import make_dout, workload_qkv
     results = []
     for knob, kn in KNOBS.items():
+        if knobs and knob not in knobs:
+            continue
         names = [variant_name(knob, v) for v in kn["values"]]
         libs = {n: binding.load_library(lib_path(n)) for n in names}
         for wl in kn["workloads"]:
@@ -238,11 +242,12 @@ def main(argv=None):
     ap.add_argument("what", choices=["build", "run"])
     ap.add_argument("--write", help="markdown file for the results table (run)")
     ap.add_argument("--jobs", type=int, default=4, help="parallel compilations (build)")
+    ap.add_argument("--knobs", nargs="*", choices=list(KNOBS), help="only these knobs")
     args = ap.parse_args(argv)
     if args.what == "build":
-        build_all(args.jobs)
+        build_all(args.jobs, args.knobs)
         return
-    res = run_all()
+    res = run_all(knobs=args.knobs)
     table = markdown(res)
     print(table)
     if args.write:
