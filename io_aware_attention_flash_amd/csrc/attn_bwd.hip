@@ -26,7 +26,10 @@
 //              tiles stream through a two-stage LDS ring.
 // P and dS enter the matrix cores in the input type (bf16 or fp16), as the
 // page casts them to the operand type; S, P, dP, dS and every accumulator
-// are fp32.
+// are fp32. In both loops every MFMA's LDS operands are read a fixed number
+// of steps ahead (mfma_pipe.h), the masking of edge tiles sits under one
+// wave-uniform branch, and the register operands are loaded completely
+// before the loop, so no wait inside it covers the tile copies in flight.
 
 #include <hip/hip_runtime.h>
 
