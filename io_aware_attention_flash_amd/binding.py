@@ -268,6 +268,12 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
     workspace (a uint8 tensor of at least bwd_workspace_bytes(B, H, Nq, d)
     bytes) is taken from torch's allocator when not given. Preallocated
     (dq, dk, dv) may be passed as `grads`.
+
+    The kernels take d = 64 or 128. Another head dim (a multiple of 8 up to
+    128) is zero-padded to the next of those: padded columns add exact
+    zeros to every score and to D = rowsum(dO * O), and their gradients are
+    zero, so the first d columns are the gradients of the unpadded problem
+    (scale defaults to 1/sqrt of the unpadded d).
     """
     if q.dim() != 4 or k.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or \
             v.shape != k.shape or (k.shape[0], k.shape[1], k.shape[3]) != \
@@ -299,6 +305,19 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
            g.device != q.device for g, x in zip(grads, (q, k, v))):
         raise ValueError("grads must be contiguous tensors shaped like q, k, v, of grad_dtype, "
                          "on q's device")
+    if d not in (64, 128):
+        if d % 8 or not 8 <= d <= 128:
+            raise ValueError("the head dim must be a multiple of 8 from 8 to 128")
+        dp = 64 if d < 64 else 128
+
+        def pad(x):
+            return torch.nn.functional.pad(x, (0, dp - d))
+
+        padded = attn_bwd(pad(q), pad(k), pad(v), pad(o), lse, pad(dout), causal, scale,
+                          grad_dtype, workspace)
+        for g, x in zip(grads, padded):
+            g.copy_(x[..., :d])
+        return dq, dk, dv
     need = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -274,6 +274,36 @@ def test_bwd_cross_attention(case):
     check_grads(got, ref, terms, extra, U[dt], "cross %s" % (case,))
 
 
+# ------------------------------------------- head dims reached by padding
+ODD_D = [
+    # (B, H, Nq, Nk, d, dtype, causal): the binding zero-pads d to 64 or 128
+    (1, 2, 200, 200, 96, "bf16", True),
+    (2, 1, 130, 130, 80, "f16", False),
+    (1, 2, 97, 97, 40, "bf16", True),
+    (1, 1, 64, 300, 112, "f16", False),
+    (1, 1, 33, 33, 8, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("case", ODD_D, ids=lambda c: "B%dH%dNq%dNk%dd%d_%s_%s" % (
+    c[:6] + ("causal" if c[6] else "full",)))
+def test_bwd_padded_head_dim(case):
+    """d outside {64, 128}: gradients of the unpadded problem, in tensors
+    of the caller's shape; O and LSE from the oracle (fp32)."""
+    B, H, Nq, Nk, d, dt, causal = case
+    _say("case", case)
+    q = make_qkv(B, H, Nq, d, dt, 1.0, seed=17)[0]
+    _, k, v = make_qkv(B, H, Nk, d, dt, 1.0, seed=18)
+    dout = make_dout(B, H, Nq, d, dt, seed=17)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, causal, scale)
+    got = gpu_bwd(q, k, v, o, lse, dout, causal, scale)
+    assert got[0].shape == q.shape and got[1].shape == k.shape and got[2].shape == v.shape
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    terms, extra = _terms(q, k, v, dout, causal, scale)
+    check_grads(got, ref, terms, extra, U[dt], "padded d %s" % (case,))
+
+
 # ------------------------------------------------ full-size, sampled rows
 
 FULL = ["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16"]

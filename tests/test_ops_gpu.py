@@ -29,6 +29,8 @@ def setup_module(module):
 @pytest.mark.parametrize("B,H,N,d,dt,causal", [
     (2, 4, 256, 64, "f16", False), (2, 4, 256, 64, "f16", True),
     (1, 3, 200, 128, "bf16", True), (1, 2, 129, 128, "bf16", False),
+    # head dims the forward's general kernel and the padded backward take
+    (1, 2, 150, 96, "bf16", True), (2, 2, 100, 40, "f16", False),
 ])
 def test_autograd_matches_oracles(B, H, N, d, dt, causal):
     print("case", B, H, N, d, dt, causal, flush=True)
