@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -285,6 +286,52 @@ def bench_softmax(args):
     print(json.dumps(res), flush=True)
 
 
+class PowerSampler:
+    """Board power and gfx clocks of GPU 0 while the timed launches run:
+    amd-smi, polled 12 times in a child process (about 3.5 s). Its first
+    reading can predate the load, so the summary takes the medians over the
+    samples from 0.5 s after the start of the timed region to its end, and
+    lists every sample (seconds from the start, W, mean gfx MHz over the
+    XCDs). The timed region should outlast the sampling (say --steps 20000)."""
+
+    CMD = ("for i in $(seq 1 12); do printf '%s ' $(date +%s.%N); "
+           "amd-smi metric -p -c -g 0 --json 2>/dev/null | tr -d '\\n'; echo; sleep 0.25; done")
+    LAG_S = 0.5
+
+    def __init__(self):
+        self.t0 = time.time()
+        self.proc = subprocess.Popen(["bash", "-c", self.CMD], stdout=subprocess.PIPE,
+                                     stderr=subprocess.DEVNULL, text=True)
+
+    def stop(self):
+        t1 = time.time()
+        out, _ = self.proc.communicate(timeout=60)
+        samples = []
+        for line in out.splitlines():
+            try:
+                stamp, body = line.split(" ", 1)
+                g = json.loads(body)
+                g = g["gpu_data"][0] if isinstance(g, dict) else g[0]
+                watts = float(g["power"]["socket_power"]["value"])
+                mhz = [float(c["clk"]["value"]) for name, c in g["clock"].items()
+                       if name.startswith("gfx_") and isinstance(c, dict) and
+                       isinstance(c.get("clk"), dict)]
+                samples.append((round(float(stamp) - self.t0, 2), watts,
+                                round(sum(mhz) / len(mhz), 1) if mhz else None))
+            except (ValueError, KeyError, IndexError, TypeError):
+                continue
+        loaded = [x for x in samples if self.LAG_S <= x[0] <= t1 - self.t0]
+
+        def med(x):
+            x = [v for v in x if v is not None]
+            return sorted(x)[len(x) // 2] if x else None
+        return {"tool": "amd-smi metric -p -c", "timed_s": round(t1 - self.t0, 2),
+                "loaded_samples": len(loaded),
+                "socket_power_w_median": med([x[1] for x in loaded]),
+                "gfx_clock_mhz_median": med([x[2] for x in loaded]),
+                "samples_s_w_mhz": samples}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -301,6 +348,9 @@ def main():
     ap.add_argument("--sm-cols", type=int, default=4096)
     ap.add_argument("--sm-dtype", default="bf16", choices=["f32", "bf16", "f16"])
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--power", action="store_true",
+                    help="forward: sample board power and gfx clocks with amd-smi during the "
+                         "timed launches (use --steps 20000 or more for a few seconds of them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -354,6 +404,7 @@ def main():
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    sampler = PowerSampler() if args.power else None
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
@@ -362,6 +413,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
+    power = sampler.stop() if sampler else None
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
@@ -396,6 +448,8 @@ def main():
     }
     if w.causal:
         res["flops_exact_triangle_per_step"] = w.flops_exact_causal()
+    if power is not None:
+        res["power"] = power
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, args.cpu_budget)
     print(json.dumps(res), flush=True)
