@@ -304,6 +304,15 @@ def test_bwd_padded_head_dim(case):
     check_grads(got, ref, terms, extra, U[dt], "padded d %s" % (case,))
 
 
+def test_bwd_head_dim_out_of_range():
+    """Head dims that padding cannot serve are refused before any launch."""
+    for d in (4, 100, 136):
+        x = torch.zeros(1, 1, 8, d, dtype=torch.bfloat16, device="cuda")
+        lse = torch.zeros(1, 1, 8, dtype=torch.float32, device="cuda")
+        with pytest.raises(ValueError):
+            binding.attn_bwd(x, x, x, x, lse, x)
+
+
 # ------------------------------------------------ full-size, sampled rows
 
 FULL = ["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16"]
