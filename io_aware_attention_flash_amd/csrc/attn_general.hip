@@ -220,17 +220,17 @@ struct GenCopy {
 
 // ------------------------------------------------- bf16 / fp16 kernel
 
-template <int D>
+template <int D, int TK_ = gen_tile_k<D>()>
 struct GenShape {
-  static constexpr int TK = gen_tile_k<D>();
+  static constexpr int TK = TK_;
   static constexpr int TILE = TK * D;
   static constexpr int STAGE = 2 * TILE;  // K, V
   static constexpr int LDS_ELEMS = 2 * STAGE;
 };
 
-template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32>
+template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, int TK = gen_tile_k<D>()>
 __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
-  using S = GenShape<D>;
+  using S = GenShape<D, TK>;
   constexpr int kTileK = S::TK;
   using Copy = GenCopy<D, kTileK>;
   constexpr int NKC = D / 16, NCB = D / 32;
@@ -508,17 +508,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_gen_f32(GenParams p) {
 
 typedef void (*GenFn)(GenParams);
 
+template <int D, bool IS_BF16, int TK>
+GenFn pick16_tk(bool causal, bool out_f32) {
+  if (causal)
+    return out_f32 ? attn_gen_16<D, IS_BF16, true, true, TK> : attn_gen_16<D, IS_BF16, true, false, TK>;
+  return out_f32 ? attn_gen_16<D, IS_BF16, false, true, TK> : attn_gen_16<D, IS_BF16, false, false, TK>;
+}
+
+// At d = 64, short key sequences take 128-key tiles: half the iterations, so
+// half the per-iteration copies and barriers, which dominate a short loop;
+// for long ones the larger LDS stages cost occupancy. Measured: +8.8% at
+// 1024 keys, -8.5% at 3000. Outputs are the same bits either way (the 32-key
+// blocks run in the same order).
+constexpr int64_t kGenShortKeys = 1024;
+
 template <int D, bool IS_BF16>
-GenFn pick16(bool causal, bool out_f32) {
-  if (causal) return out_f32 ? attn_gen_16<D, IS_BF16, true, true> : attn_gen_16<D, IS_BF16, true, false>;
-  return out_f32 ? attn_gen_16<D, IS_BF16, false, true> : attn_gen_16<D, IS_BF16, false, false>;
+GenFn pick16(bool causal, bool out_f32, int64_t Nk) {
+#ifndef ATTN_CFG_GEN_TILE_K
+  if constexpr (D == 64)
+    if (Nk <= kGenShortKeys) return pick16_tk<D, IS_BF16, 128>(causal, out_f32);
+#endif
+  (void)Nk;
+  return pick16_tk<D, IS_BF16, gen_tile_k<D>()>(causal, out_f32);
 }
 
 template <int D>
-GenFn pick(attn_dtype in, bool causal, bool out_f32) {
+GenFn pick(attn_dtype in, bool causal, bool out_f32, int64_t Nk) {
   if (in == ATTN_F32) return causal ? attn_gen_f32<D, true> : attn_gen_f32<D, false>;
-  if (in == ATTN_BF16) return pick16<D, true>(causal, out_f32);
-  return pick16<D, false>(causal, out_f32);
+  if (in == ATTN_BF16) return pick16<D, true>(causal, out_f32, Nk);
+  return pick16<D, false>(causal, out_f32, Nk);
 }
 
 int elem_bytes(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
@@ -598,7 +616,8 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
   const double qk = (double)scale * 1.4426950408889634;
   p.qk = qk < (double)FLT_MIN ? FLT_MIN : (float)qk;
   const bool out_f32 = out_dtype == ATTN_F32;
-  GenFn fn = d <= 64 ? pick<64>(in_dtype, causal != 0, out_f32) : pick<128>(in_dtype, causal != 0, out_f32);
+  GenFn fn = d <= 64 ? pick<64>(in_dtype, causal != 0, out_f32, Nk)
+                     : pick<128>(in_dtype, causal != 0, out_f32, Nk);
   void *args[] = {&p};
   const hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)grid),
                                          dim3(kThreads), args, 0, (hipStream_t)stream);

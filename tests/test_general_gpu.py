@@ -52,6 +52,9 @@ CROSS = [
     (2, 3, 300, 77, 128, "bf16", 1.0), (1, 2, 64, 1000, 64, "f16", 1.0),
     (1, 1, 129, 257, 128, "bf16", 3.0), (2, 2, 1, 1, 8, "f16", 1.0),
     (1, 2, 200, 130, 96, "f32", 1.0),
+    # d <= 64 takes 128-key tiles up to 1024 keys and 64-key tiles past that
+    (1, 2, 100, 1024, 64, "bf16", 1.0), (1, 2, 100, 1025, 64, "f16", 1.0),
+    (1, 1, 70, 1500, 48, "bf16", 2.0),
 ]
 
 
