@@ -66,6 +66,34 @@ def measured_traffic(workload, out_dtype):
     return ent.get("hbm_bytes_per_launch")
 
 
+def flushed_timing(step, stream, launches, flush_mb):
+    """Per-launch times with the caches cold: before each launch, write a
+    `flush_mb` MiB buffer (more than the 4 MB L2 of every XCD and the 256 MB
+    Infinity Cache), then time that launch alone with events on its stream.
+    Returns the median, the interquartile range and the extremes in ms."""
+    buf = torch.empty(flush_mb << 20, dtype=torch.uint8, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(launches)]
+    for i, (a, b) in enumerate(evs):
+        buf.fill_(i & 0xFF)
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+
+    def q(f):
+        x = f * (len(ts) - 1)
+        lo = int(x)
+        hi = min(lo + 1, len(ts) - 1)
+        return ts[lo] + (ts[hi] - ts[lo]) * (x - lo)
+    del buf
+    return {"launches": launches, "flush_bytes": flush_mb << 20, "median_ms": round(q(0.5), 5),
+            "p25_ms": round(q(0.25), 5), "p75_ms": round(q(0.75), 5),
+            "iqr_ms": round(q(0.75) - q(0.25), 5), "min_ms": round(ts[0], 5),
+            "max_ms": round(ts[-1], 5)}
+
+
 def cpu_baseline(w, q, k, v, budget_s=12.0):
     """Time the fp64 oracle on whole heads of the same inputs until about
     `budget_s` seconds of CPU work; report the FLOP rate of that sample."""
@@ -351,6 +379,11 @@ def main():
     ap.add_argument("--power", action="store_true",
                     help="forward: sample board power and gfx clocks with amd-smi during the "
                          "timed launches (use --steps 20000 or more for a few seconds of them)")
+    ap.add_argument("--flush", type=int, default=0, metavar="LAUNCHES",
+                    help="forward: after the timed region, also time LAUNCHES single launches "
+                         "each preceded by a write of --flush-mb MiB (cold L2 and Infinity "
+                         "Cache); report their median and interquartile range")
+    ap.add_argument("--flush-mb", type=int, default=512)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB --steps times (reference "
                          "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -370,8 +403,7 @@ def main():
               "(every (batch, head) is independent; see the sharding notes in the design doc). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.which == "bwd":
         bench_bwd(args)
@@ -450,6 +482,10 @@ def main():
         res["flops_exact_triangle_per_step"] = w.flops_exact_causal()
     if power is not None:
         res["power"] = power
+    if args.flush > 0:
+        fl = flushed_timing(step, stream, args.flush, args.flush_mb)
+        fl["tflops_at_median"] = round(flops / (fl["median_ms"] * 1e-3) / 1e12, 2)
+        res["flushed"] = fl
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, qc, kc, vc, args.cpu_budget)
     print(json.dumps(res), flush=True)

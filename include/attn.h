@@ -69,9 +69,24 @@ typedef enum {
  *           (BF16, BF16) (BF16, F32) (F16, F16) (F16, F32) (F32, F32).
  *           bf16 and fp16 inputs are multiplied on the matrix cores with fp32
  *           accumulation; the softmax weights P enter the P.V product as
- *           fp16 (for bf16 inputs V is converted to fp16, which is exact for
- *           |v| in [2^-14, 65504]); softmax statistics are fp32. fp32 inputs
- *           are computed in fp32 throughout.
+ *           fp16 (for bf16 inputs V is converted to fp16); softmax
+ *           statistics are fp32. fp32 inputs are computed in fp32
+ *           throughout.
+ *           bf16 V of any finite magnitude is accepted:
+ *            - |v| in [2^-14, 65504]: the fp16 copy is exact.
+ *            - |v| > 65504: its fp16 copy is infinite, which makes the
+ *              accumulators of the rows that meet it non-finite. The kernel
+ *              checks every accumulator after the key loop and recomputes
+ *              those rows with P rounded to bf16 against the bf16 V (the
+ *              page's own operand precision), reading K and V from memory.
+ *              Correct, but much slower for the rows concerned. The fp32
+ *              accumulators bound |O| sums: max|v| * 2^8 * N must stay
+ *              below fp32's range.
+ *            - |v| < 2^-14: fp16's subnormal range; the copy is rounded to a
+ *              multiple of 2^-24, so each output element moves by at most
+ *              2^-25 (the weights of a row are non-negative and sum to 1).
+ *           LSE does not depend on V and is the same in every case. Inputs
+ *           holding inf or NaN give non-finite outputs.
  * stream  : hipStream_t (or NULL). The call only enqueues work and does not
  *           synchronise; a fault during execution surfaces at the caller's
  *           next synchronisation.
@@ -193,9 +208,10 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
 
 /*
  * attn_fwd_strided -- the attention forward of attn_fwd for general layouts:
- * Nq query rows against Nk keys per head (cross-attention; the pages'
- * "Triton Kernel Practice" checks its kernel on mismatched query and key
- * lengths), any head dimension d = 8, 16, ..., 128 (computed at 64 or 128
+ * Nq query rows against Nk keys per head (cross-attention; the page
+ * "Programming an attention kernel in Triton", section "Kernel 4: bringing
+ * it together, a self-attention kernel", checks its kernel on mismatched
+ * query and key lengths), any head dimension d = 8, 16, ..., 128 (computed at 64 or 128
  * with zero-padded columns, exact by "4.4 Writing GPU Kernels with Triton",
  * section "Sizing the attention kernel"), and strided tensors.
  *

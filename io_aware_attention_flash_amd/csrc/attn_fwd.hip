@@ -59,7 +59,8 @@ constexpr int kBlockM = 128;  // query rows per workgroup (32 per wave)
 struct FwdParams {
   const void *q;
   const void *k;
-  const void *v;
+  const void *v;     // V as the kernel reads it (the fp16 copy when a first pass made one)
+  const void *v_in;  // V as the caller passed it
   void *o;
   float *lse;
   int N;         // sequence length
@@ -708,6 +709,92 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
 #undef ITER
 }
 
+// bf16 V outside fp16's finite range. The P.V product runs on fp16 copies
+// of bf16 V, so a value with |v| > 65504 became +-inf there and the
+// accumulators of every wave that met it are not finite. Such a wave then
+// recomputes its rows' outputs the way the page's kernel does, with P
+// rounded to bf16 and V as the caller gave it (bf16 x bf16 on the matrix
+// cores, fp32 accumulation), reading K and V straight from memory, against
+// the final reference maximum: every score is within 2^kRescaleLog2 of it,
+// so every weight stays <= 2^8. The rows' log-sum-exp is unchanged (it does
+// not depend on V); the returned sum of the bf16-rounded weights normalises
+// the new output. Inputs holding inf or NaN give non-finite outputs either
+// way.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, size_t head, int r0, int qrow,
+                                                int g, int l32, const u32x4 *qf,
+                                                RowState16<D> &st) {
+  constexpr int NKC = D / 16, NCB = D / 32;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const int N = p.N;
+  const uint16_t *Kh = static_cast<const uint16_t *>(p.k) + head;
+  const uint16_t *Vh = static_cast<const uint16_t *>(p.v_in) + head;
+  const int kend = CAUSAL ? min(N, r0 + 32) : N;
+  const float qk = p.qk, neg_m = st.neg_m;
+  float l = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) st.acc[cb] = f32x16{};
+#pragma unroll 1
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    // S^T for keys k0 .. k0 + 31 (K operand row k0 + l32, as k_frag lays it out)
+    const int key = k0 + l32;
+    const uint16_t *krow = Kh + (size_t)(key < N ? key : 0) * D + 8 * g;
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + 16 * kc);
+      if (key >= N) kf = u32x4{0, 0, 0, 0};
+      sc = mfma_qk<true>(kf, qf[kc], sc);
+    }
+    // weights, rounded to bf16 and packed as the P^T operands of the two
+    // 16-key steps; the row sum takes the rounded values
+    uint32_t pb[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      float w[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kk = score_key(k0, 0, e + i, g);
+        const bool dead = kk >= N || (CAUSAL && kk > qrow);
+        w[i] = dead ? 0.f : exp2_fast(fmaf(sc[e + i], qk, neg_m));
+      }
+      const bf16x2 h = {(__bf16)w[0], (__bf16)w[1]};
+      l += (float)h[0] + (float)h[1];
+      pb[e >> 1] = __builtin_bit_cast(uint32_t, h);
+    }
+    // O^T += V^T P^T: the V^T operand of step (t, cb) is column 32cb + l32
+    // at keys k0 + 16t + 8u + 4g + i (value 4u + i), loaded element by element
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pf = {pb[4 * t], pb[4 * t + 1], pb[4 * t + 2], pb[4 * t + 3]};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        uint32_t vv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int kk = k0 + 16 * t + 8 * (x >> 2) + 4 * g + (x & 3);
+          vv[x] = kk < N ? Vh[(size_t)kk * D + 32 * cb + l32] : 0u;
+        }
+        const u32x4 a = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
+                         vv[6] | (vv[7] << 16)};
+        st.acc[cb] = mfma_qk<true>(a, pf, st.acc[cb]);
+      }
+    }
+  }
+  return l;
+}
+
+// Whether any accumulator of this lane is inf or NaN.
+template <int D>
+__device__ __forceinline__ bool acc_not_finite(const RowState16<D> &st) {
+  bool bad = false;
+#pragma unroll
+  for (int cb = 0; cb < D / 32; ++cb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(st.acc[cb][r]);
+  return bad;
+}
+
 // Row-major staging of one wave's 32 x D block of O in LDS for the
 // epilogue: E bytes per element, rows of ROWB bytes (a whole row of O, or a
 // MAXROWB-byte part of it when longer: PASSES parts), CPR 16-byte chunks per row,
@@ -768,7 +855,8 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
     pp.k_dma[c] = dma_offset<D, false>(tid) + c * S::INS_BYTES;
     pp.v_dma[c] = dma_offset<D, true>(tid) + c * S::INS_BYTES;
   }
-  // This lane's query row; rows past N use row N-1's data and are never stored.
+  // This lane's query row. Rows past N read zeros (the query tile's copy
+  // descriptor is cut at N) and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
   pp.qrow = r0 + l32;
 
@@ -839,9 +927,13 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   // Epilogue: combine the two key halves of the row sum, divide once, LSE.
   const float l_tot = sum_halves(st.l);
   const float l_safe = l_tot > 0.f ? l_tot : 1.f;
-  const float inv = 1.0f / l_safe;
+  float inv = 1.0f / l_safe;
   if (pp.qrow < N && g == 0)
     p.lse[(size_t)bh * N + pp.qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
+  if (IS_BF16 && __any(acc_not_finite<D>(st))) {
+    const float lb = sum_halves(redo_rows_bf16<D, CAUSAL>(p, head, r0, pp.qrow, g, l32, qf, st));
+    inv = 1.0f / (lb > 0.f ? lb : 1.f);
+  }
   // O leaves through LDS. A lane holds one row, so stores straight from the
   // accumulators would touch 64 rows (64 cache lines) per instruction; staged
   // row-major, each store instruction writes whole lines. Each wave uses its
@@ -1160,6 +1252,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   p.q = q;
   p.k = k;
   p.v = v;
+  p.v_in = v;
   p.o = o;
   p.lse = lse;
   p.N = (int)N;

@@ -1,13 +1,14 @@
 // General-layout attention forward for gfx950 (MI355X): the same operation
 // as attn_fwd, for the cases its tuned kernels do not take:
-//  - a different number of keys than queries (cross-attention; the test
-//    section of "Triton Kernel Practice" checks the kernel on mismatched
-//    query and key lengths);
+//  - a different number of keys than queries (cross-attention;
+//    "Programming an attention kernel in Triton", section "Kernel 4:
+//    bringing it together, a self-attention kernel", checks its kernel on
+//    mismatched query and key lengths);
 //  - head dimensions d <= 128 other than 64 and 128, multiple of 8, computed
-//    at D = 64 or 128 with the extra columns read as zeros ("4.4 Writing GPU
-//    Kernels with Triton", section "Sizing the attention kernel": zero-padding
-//    the head dimension is exact -- the padded columns add 0 to every score
-//    and give output columns that are not stored);
+//    at D = 64 or 128 with the extra columns read as zeros (the padding note
+//    of "4.4 Writing GPU Kernels with Triton", section "Sizing the attention
+//    kernel"). This changes nothing: a zero column contributes 0 to every
+//    dot product q.k, and the output columns past d are never written;
 //  - strided tensors: element (b, h, n, c) at b*sb + h*sh + n*sn + c (the
 //    Triton kernels of the same pages take per-dimension strides).
 //
@@ -218,6 +219,76 @@ struct GenCopy {
   }
 };
 
+// ------------------------------------------ bf16 V beyond fp16's range
+
+// The P.V product runs on fp16 copies of bf16 V, so a value with
+// |v| > 65504 became +-inf there and the accumulators of every wave that met
+// it are not finite. Such a wave recomputes its rows' outputs the way the
+// page's kernel does: P rounded to bf16, V as given, bf16 x bf16 on the
+// matrix cores with fp32 accumulation, K and V read straight from memory
+// (strided, columns past d as zeros), against the final reference maximum m
+// (every score is within 2^8 of it, so every weight is <= 2^8). Returns this
+// lane's sum of the bf16-rounded weights; acc is overwritten.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ float redo_rows_bf16(const GenParams &p, const uint16_t *Kh,
+                                                const uint16_t *Vh, int qw0, int qrow, int g,
+                                                int l32, const u32x4 *qf, float m,
+                                                f32x16 (&acc)[D / 32]) {
+  constexpr int NKC = D / 16, NCB = D / 32;
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const int Nk = p.Nk, d = p.d;
+  const int64_t ks = p.ks[2], vs = p.vs[2];
+  const int kend = CAUSAL ? min(Nk, qw0 + 32) : Nk;
+  const float qk = p.qk, mref = m == -INFINITY ? 0.f : m;
+  float l = 0.f;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x16{};
+#pragma unroll 1
+  for (int k0 = 0; k0 < kend; k0 += 32) {
+    const int key = k0 + l32;
+    const uint16_t *krow = Kh + (int64_t)(key < Nk ? key : 0) * ks + 8 * g;
+    f32x16 sc = f32x16{};
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      u32x4 kf = u32x4{0, 0, 0, 0};
+      if (key < Nk && 16 * kc + 8 * g < d) kf = *reinterpret_cast<const u32x4 *>(krow + 16 * kc);
+      sc = mfma_in<true>(kf, qf[kc], sc);
+    }
+    uint32_t pb[8];
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      float w[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int kk = k0 + 8 * ((e + i) >> 2) + 4 * g + ((e + i) & 3);
+        const bool dead = kk >= Nk || (CAUSAL && kk > qrow);
+        w[i] = dead ? 0.f : __builtin_amdgcn_exp2f(sc[e + i] * qk - mref);
+      }
+      const bf16x2 hh = {(__bf16)w[0], (__bf16)w[1]};
+      l += (float)hh[0] + (float)hh[1];
+      pb[e >> 1] = __builtin_bit_cast(uint32_t, hh);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const u32x4 pf = {pb[4 * t], pb[4 * t + 1], pb[4 * t + 2], pb[4 * t + 3]};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int col = 32 * cb + l32;
+        uint32_t vv[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const int kk = k0 + 16 * t + 8 * (x >> 2) + 4 * g + (x & 3);
+          vv[x] = kk < Nk && col < d ? Vh[(int64_t)kk * vs + col] : 0u;
+        }
+        const u32x4 a = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
+                         vv[6] | (vv[7] << 16)};
+        acc[cb] = mfma_in<true>(a, pf, acc[cb]);
+      }
+    }
+  }
+  return l;
+}
+
 // ------------------------------------------------- bf16 / fp16 kernel
 
 template <int D, int TK_ = gen_tile_k<D>()>
@@ -369,7 +440,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_gen_16(GenParams p) {
 
   const float l_tot = l + __shfl_xor(l, 32);
   const float l_safe = l_tot > 0.f ? l_tot : 1.f;
-  const float inv = 1.0f / l_safe;
+  float inv = 1.0f / l_safe;
+  // bf16 V with |v| > 65504 became +-inf in its fp16 copy: recompute this
+  // wave's outputs with bf16 P against the given V (see redo_rows_bf16).
+  if (IS_BF16) {
+    bool bad = false;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bad |= !__builtin_isfinite(acc[cb][r]);
+    if (__any(bad)) {
+      const float lb = redo_rows_bf16<D, CAUSAL>(p, Kh, Vh, qw0, qrow, g, l32, qf, m, acc);
+      const float lt = lb + __shfl_xor(lb, 32);
+      inv = 1.0f / (lt > 0.f ? lt : 1.f);
+    }
+  }
   if (qrow < Nq) {
     if (g == 0)
       p.lse[(size_t)bh * Nq + qrow] =

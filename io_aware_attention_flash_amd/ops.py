@@ -35,7 +35,9 @@ def _fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
 
 @_fwd.register_fake
 def _fwd_fake(q, k, v, causal, scale):
-    return torch.empty_like(q), q.new_empty(q.shape[:3], dtype=torch.float32)
+    # The real op returns fresh contiguous tensors whatever the input strides
+    # (empty_like would copy the strides of a transposed view).
+    return q.new_empty(q.shape), q.new_empty(q.shape[:3], dtype=torch.float32)
 
 
 @torch.library.custom_op(_NS + "::bwd", mutates_args=())
@@ -48,7 +50,7 @@ def _bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse
 
 @_bwd.register_fake
 def _bwd_fake(q, k, v, o, lse, dout, causal, scale):
-    return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    return q.new_empty(q.shape), k.new_empty(k.shape), v.new_empty(v.shape)
 
 
 def _setup_context(ctx, inputs, output):

@@ -22,8 +22,6 @@ import concurrent.futures
 import ctypes
 import json
 import os
-import subprocess
-import sys
 import time
 
 from . import build as hipbuild
@@ -83,19 +81,9 @@ def lib_path(name):
 
 
 def _build_one(name, defs):
-    hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     out = lib_path(name)
-    cmd = [hipcc] + hipbuild.HIPCC_FLAGS + defs + ["-I", hipbuild.INCLUDE] + hipbuild.SRCS + \
-        ["-o", out]
     t0 = time.time()
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stderr[-4000:])
-        raise RuntimeError("hipcc failed for %s" % name)
-    bad = hipbuild.scratch_users(res.stderr)
-    if bad:
-        os.remove(out)
-        raise RuntimeError("%s: kernels use scratch memory: %s" % (name, bad))
+    hipbuild.build(extra=defs, out=out, jobs=2)
     return "built %-28s %s (%.0f s)" % (name, " ".join(defs) or "(shipped)", time.time() - t0)
 
 

@@ -33,8 +33,9 @@
  * first (three passes per row, as in the forward's stable softmax).
  *
  * A head has Nq query rows and Nk keys; they differ for cross-attention
- * (which "Triton Kernel Practice" tests its kernel on), where the causal
- * mask is not defined.
+ * (which "Programming an attention kernel in Triton", section "Kernel 4:
+ * bringing it together, a self-attention kernel", tests its kernel on),
+ * where the causal mask is not defined.
  */
 #include <math.h>
 #include <stdint.h>

@@ -79,8 +79,10 @@ static void oracle_one_row(const double *q, const double *k, const double *v,
 
 /*
  * attn_oracle_rows_qk -- attention for a list of query rows, with Nq query
- * rows and Nk keys per head (cross-attention when they differ; the
- * "Triton Kernel Practice" page validates its kernel on such shapes). The
+ * rows and Nk keys per head (cross-attention when they differ; the page
+ * "Programming an attention kernel in Triton", section "Kernel 4: bringing
+ * it together, a self-attention kernel", validates its kernel on such
+ * shapes). The
  * causal mask (query i sees keys j <= i) is defined here for Nq == Nk only.
  *
  * q        : [B][H][Nq][d] row-major fp64;  k, v : [B][H][Nk][d] (callers

@@ -266,8 +266,9 @@ def check_row_subsets(grads):
 
 
 def check_cross_attention(grads):
-    """Query and key lengths that differ (the shapes "Triton Kernel Practice"
-    validates its forward on, and more): torch's fp64 autograd, every element
+    """Query and key lengths that differ (the shapes "Programming an attention
+    kernel in Triton", section "Kernel 4: bringing it together, a
+    self-attention kernel", validates its forward on, and more): torch's fp64 autograd, every element
     against central finite differences of the forward oracle on a tiny
     case, and the Jacobian invariants."""
     for t, (B, H, nq, nk, d) in enumerate([(1, 1, 5, 15, 32), (1, 1, 1, 10, 64), (2, 3, 7, 19, 8)]):

@@ -253,8 +253,9 @@ def check_row_subset(attn):
 
 
 def check_cross_attention(attn):
-    """Query and key lengths that differ ("Triton Kernel Practice" validates
-    its kernel on Q (5, 32) against K, V (15, 32) and on a single query
+    """Query and key lengths that differ ("Programming an attention kernel in
+    Triton", section "Kernel 4: bringing it together, a self-attention
+    kernel", validates its kernel on Q (5, 32) against K, V (15, 32) and on a single query
     against 10 keys): agreement with torch's fp64 scaled_dot_product_attention
     and with the brute-force two-pass and online variants, at the page's
     shapes and a few more."""

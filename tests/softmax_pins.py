@@ -17,7 +17,8 @@ def _close(a, b, tol, what):
 
 def check_torch(softmax):
     """torch's fp64 CPU softmax, on the page's test shape (1823 x 781) and on
-    the 2000-column case of the "Triton Kernel Practice" bug story."""
+    the 2000-column case of the bug story in "Programming an attention kernel
+    in Triton", section "Kernel 3: fused softmax, and the bug that mattered"."""
     for t, shape in enumerate([(1823, 781), (4, 5), (3, 2000), (7, 1)]):
         x = _rand(shape, 300 + t, 2.0)
         ref = torch.softmax(torch.from_numpy(x), dim=1).numpy()

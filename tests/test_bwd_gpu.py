@@ -42,8 +42,7 @@ DT = {"f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def setup_module(module):
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 

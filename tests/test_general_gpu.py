@@ -20,8 +20,7 @@ DEV = torch.device("cuda:0")
 
 
 def setup_module(module):
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 

@@ -22,3 +22,19 @@ def test_fake_shapes():
         assert lse.shape == (2, 3, 17) and lse.dtype == torch.float32
         dq, dk, dv = torch.ops.io_aware_attention_flash.bwd(q, q, q, o, lse, q, True, 0.125)
         assert dq.shape == dk.shape == dv.shape == q.shape
+
+
+def test_fake_outputs_are_contiguous_for_strided_inputs():
+    """The real ops return fresh contiguous tensors, so the fakes must too:
+    a [B, N, H, d] tensor seen as [B, H, N, d] (a transposed view) must not
+    hand its strides to the outputs."""
+    with FakeTensorMode():
+        x = torch.empty(2, 17, 3, 64, dtype=torch.bfloat16)
+        q = x.transpose(1, 2)
+        assert not q.is_contiguous()
+        o, lse = torch.ops.io_aware_attention_flash.fwd(q, q, q, False, 0.125)
+        assert o.is_contiguous() and o.stride() == (3264, 1088, 64, 1)
+        assert lse.is_contiguous()
+        grads = torch.ops.io_aware_attention_flash.bwd(q, q, q, o, lse, q, False, 0.125)
+        for g in grads:
+            assert g.shape == q.shape and g.is_contiguous()

@@ -21,8 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def setup_module(module):
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 
@@ -86,6 +85,22 @@ def test_opcheck():
     torch.library.opcheck(torch.ops.io_aware_attention_flash.fwd.default, (q, k, v, True, 0.125),
                           test_utils=("test_schema", "test_faketensor",
                                       "test_autograd_registration"))
+
+
+def test_opcheck_transposed_views():
+    """The same checks on [B, N, H, d] tensors seen as [B, H, N, d]: the fake
+    outputs must carry the real outputs' (contiguous) strides."""
+    q, k, v = (x.cuda().transpose(1, 2).contiguous().transpose(1, 2)
+               for x in make_qkv(1, 2, 64, 64, "bf16", 1.0, seed=23))
+    assert not q.is_contiguous()
+    torch.library.opcheck(torch.ops.io_aware_attention_flash.fwd.default, (q, k, v, False, 0.125),
+                          test_utils=("test_schema", "test_faketensor",
+                                      "test_autograd_registration"))
+    o, lse = torch.ops.io_aware_attention_flash.fwd(q, k, v, False, 0.125)
+    dout = torch.randn_like(o)
+    torch.library.opcheck(torch.ops.io_aware_attention_flash.bwd.default,
+                          (q, k, v, o, lse, dout, False, 0.125),
+                          test_utils=("test_schema", "test_faketensor"))
 
 
 def test_training_step_runs():

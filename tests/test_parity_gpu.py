@@ -24,8 +24,7 @@ DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def setup_module(module):
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 
@@ -107,6 +106,42 @@ def test_parity_full(case):
     ref_o, ref_l = oracle.attn_oracle(q, k, v, causal=causal, scale=sc)
     o, lse = gpu_attn(q, k, v, causal, sc)
     check_close(o.numpy(), lse.numpy(), ref_o, ref_l, str(case))
+
+
+# ------------------------------------------- the named workloads, every element
+FULL_WORKLOAD_CASES = [(name, 0) for name in WORKLOADS] + [
+    ("b2h32_n4096_d128_bf16_causal", 1), ("b2h32_n4096_d128_bf16_causal", 2)]
+
+
+def _log_parity(record):
+    """Append one JSON line per compared workload to $ATTN_PARITY_LOG, when set."""
+    path = os.environ.get("ATTN_PARITY_LOG")
+    if path:
+        import json
+        with open(path, "a") as f:
+            f.write(json.dumps(record) + "\n")
+
+
+@pytest.mark.parametrize("name,seed", FULL_WORKLOAD_CASES,
+                         ids=["%s_seed%d" % c for c in FULL_WORKLOAD_CASES])
+def test_parity_workload_full(name, seed):
+    """Every element of O (fp32 output) and of LSE of a named workload against
+    the oracle: max and mean |err| over all B*H*N*d outputs, max |err| over
+    all B*H*N log-sum-exps, at the launch configuration bench.py times."""
+    w = WORKLOADS[name]
+    _say("full workload", name, "seed", seed)
+    q, k, v = workload_qkv(w, seed=seed)
+    o, lse = gpu_attn(q, k, v, w.causal, w.scale)
+    ref_o, ref_l = oracle.attn_oracle(q, k, v, causal=w.causal, scale=w.scale)
+    o = o.numpy().astype(np.float64)
+    lse = lse.numpy().astype(np.float64)
+    err = np.abs(o - ref_o)
+    lerr = np.abs(lse - ref_l)
+    rec = {"workload": name, "seed": seed, "elements": int(err.size), "rows": int(lerr.size),
+           "o_max_abs": float(err.max()), "o_mean_abs": float(err.mean()),
+           "lse_max_abs": float(lerr.max())}
+    _log_parity(rec)
+    check_close(o, lse, ref_o, ref_l, "%s seed %d (all %d elements)" % (name, seed, err.size))
 
 
 # ---------------------------------------------- the named workloads, sampled

@@ -27,8 +27,7 @@ SUBNORMAL = {"f32": 0.0, "bf16": 0.0, "f16": 2.0 ** -25}
 
 
 def setup_module(module):
-    if not os.path.exists(binding.LIB_PATH):
-        hipbuild.build()
+    hipbuild.ensure_built()
     assert torch.cuda.is_available(), "GPU tests need a GPU"
 
 
