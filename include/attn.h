@@ -44,11 +44,12 @@ typedef enum {
   ATTN_ERR_UNSUPPORTED = 3,  /* head dim or dtype combination not built */
   ATTN_ERR_SCALE = 4,        /* scale is NaN, infinite or negative */
   ATTN_ERR_HIP = 5,          /* the HIP runtime reported an error at launch */
-  ATTN_ERR_WORKSPACE = 6     /* a required workspace is NULL, too small or misaligned */
+  ATTN_ERR_WORKSPACE = 6,    /* a required workspace is NULL, too small or misaligned */
+  ATTN_ERR_CAPACITY = 7      /* larger than the allocation-free entry point's static scratch */
 } attn_status;
 
 /* Version of this ABI (bumped on any incompatible change). */
-#define ATTN_ABI_VERSION 1
+#define ATTN_ABI_VERSION 2
 
 /*
  * attn_fwd -- enqueue the attention forward on `stream`.
@@ -205,6 +206,29 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
                         float scale, attn_dtype in_dtype, attn_dtype o_dtype,
                         attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd_qk without a workspace argument and without
+ * any allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The 8 bytes per query row that attn_bwd_qk keeps in the caller's workspace
+ * live instead in a static device array of 16 MiB inside the library (one
+ * per GPU, held until the process ends), so B*H*Nq may be at most 2^21;
+ * larger problems return ATTN_ERR_CAPACITY before any HIP call. The array's
+ * device address is looked up (hipGetSymbolAddress) on the first call on
+ * each device, which must be the current device. Nothing in it needs to
+ * start at zero: every call writes each row it reads first. Calls that
+ * overlap on one GPU (other streams, other threads) share the array and
+ * race; serialise them. Every other argument, check, error and result is
+ * that of attn_bwd_qk: the same kernels run, so the gradients are bitwise
+ * the same.
+ */
+attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                             attn_dtype grad_dtype, void *stream);
 
 /*
  * attn_fwd_strided -- the attention forward of attn_fwd for general layouts:

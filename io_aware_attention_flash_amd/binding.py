@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
 # attn_dtype / attn_status values of include/attn.h
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
-          4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE"}
+          4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_CAPACITY"}
 EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_fwd_strided", "attn_bwd",
-           "attn_bwd_qk",
+           "attn_bwd_qk", "attn_bwd_noalloc",
            "attn_bwd_workspace_bytes", "attn_row_softmax", "attn_status_string", "attn_abi_version",
            "attn_last_hip_error")
 
@@ -64,6 +64,10 @@ def load_library(path=LIB_PATH):
     lib.attn_bwd_qk.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                 ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                     ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_int, vp]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -251,6 +255,16 @@ def attn_bwd_qk_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr,
                                       dv_ptr, int(B), int(H), int(Nq), int(Nk), int(d),
                                       int(bool(causal)), float(scale), int(in_dtype), int(o_dtype),
                                       int(grad_dtype), ws_ptr, int(ws_bytes), stream)
+
+
+def attn_bwd_noalloc_raw(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr, dk_ptr, dv_ptr, B, H,
+                         Nq, Nk, d, causal, scale, in_dtype, o_dtype, grad_dtype, stream=None):
+    """Direct call of attn_bwd_noalloc (no workspace, no allocation); returns
+    the status."""
+    return load_library().attn_bwd_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, do_ptr, dq_ptr,
+                                           dk_ptr, dv_ptr, int(B), int(H), int(Nq), int(Nk),
+                                           int(d), int(bool(causal)), float(scale), int(in_dtype),
+                                           int(o_dtype), int(grad_dtype), stream)
 
 
 def bwd_workspace_bytes(B, H, N, d):

@@ -37,6 +37,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "attn.h"
 #include "mfma_pipe.h"
 
@@ -659,23 +661,12 @@ size_t ws_bytes(int64_t B, int64_t H, int64_t N) {
   return (((size_t)(B * H) * (size_t)N * 8) + 255) & ~(size_t)255;
 }
 
-}  // namespace
-
-extern "C" {
-
-size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  if (B < 1 || H < 1 || N < 1 || N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return 0;
-  if (d != 64 && d != 128) return 0;
-  return ws_bytes(B, H, N);
-}
-
-attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void *o,
-                        const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                        float scale, attn_dtype in_dtype, attn_dtype o_dtype,
-                        attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
-                        void *stream) {
-  // Validation first: no HIP call happens before every argument is checked.
+// Argument checks shared by the backward's entry points; no HIP call.
+attn_status bwd_check(const void *q, const void *k, const void *v, const void *o,
+                      const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                      float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                      attn_dtype grad_dtype) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1) return ATTN_ERR_SHAPE;
   if (Nq > (int64_t(1) << 24) || Nk > (int64_t(1) << 24) || B * H > (int64_t(1) << 24))
@@ -686,9 +677,16 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
   if (o_dtype != in_dtype && o_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (grad_dtype != in_dtype && grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  const size_t need = ws_bytes(B, H, Nq);
-  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
-    return ATTN_ERR_WORKSPACE;
+  return ATTN_OK;
+}
+
+// The three launches, with LD rows (8 bytes per query row) at `ld`. Checks
+// the launch sizes before any HIP call.
+attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
+                    const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                    float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                    attn_dtype grad_dtype, void *ld, void *stream) {
   const int64_t nkb = (Nk + kBlockK - 1) / kBlockK, nqb = (Nq + kBlockQ - 1) / kBlockQ;
   const int64_t rows = B * H * Nq;
   const int64_t lpr = d / 8;
@@ -706,7 +704,7 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
-  p.ld = reinterpret_cast<f32x2 *>(workspace);
+  p.ld = reinterpret_cast<f32x2 *>(ld);
   p.Nq = (int)Nq;
   p.Nk = (int)Nk;
   p.BH = (int)(B * H);
@@ -743,6 +741,84 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+// The allocation-free backward (attn_bwd_noalloc) keeps its LD rows in this
+// array instead of a caller's workspace: one copy per GPU, held until the
+// process ends. Host code never uses the name itself (on the host it is a
+// stand-in, not a device address): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kScratchBytes = size_t(16) << 20;  // 2^21 query rows of 8 bytes
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on first use).
+attn_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess && (dev < 0 || dev >= kMaxDevices)) err = hipErrorInvalidDevice;
+  if (err != hipSuccess) {
+    attn_internal::set_last_hip_error((int)err);
+    return ATTN_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || !ptr) {
+      attn_internal::set_last_hip_error((int)(err != hipSuccess ? err : hipErrorInvalidSymbol));
+      return ATTN_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return 0;
+  if (d != 64 && d != 128) return 0;
+  return ws_bytes(B, H, N);
+}
+
+attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void *o,
+                        const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                        float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                        attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream) {
+  // Validation first: no HIP call happens before every argument is checked.
+  attn_status st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale,
+                             in_dtype, o_dtype, grad_dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = ws_bytes(B, H, Nq);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return ATTN_ERR_WORKSPACE;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, in_dtype,
+                 o_dtype, grad_dtype, workspace, stream);
+}
+
+attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const void *o,
+                             const float *lse, const void *dout, void *dq, void *dk, void *dv,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                             float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                             attn_dtype grad_dtype, void *stream) {
+  attn_status st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale,
+                             in_dtype, o_dtype, grad_dtype);
+  if (st != ATTN_OK) return st;
+  if (ws_bytes(B, H, Nq) > kScratchBytes) return ATTN_ERR_CAPACITY;
+  void *ld = nullptr;
+  st = scratch_address(&ld);
+  if (st != ATTN_OK) return st;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, in_dtype,
+                 o_dtype, grad_dtype, ld, stream);
 }
 
 attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

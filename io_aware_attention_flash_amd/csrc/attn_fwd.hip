@@ -1220,6 +1220,7 @@ const char *attn_status_string(attn_status s) {
     case ATTN_ERR_SCALE: return "scale must be finite and >= 0";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
     case ATTN_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
+    case ATTN_ERR_CAPACITY: return "problem larger than the static scratch of the allocation-free entry point";
   }
   return "unknown status";
 }

@@ -223,3 +223,23 @@ def test_bwd_qk_error_paths_need_no_gpu(lib, args, code):
     st = binding.attn_bwd_qk_raw(P, P, P, P, P, P, P, P, P, a["B"], a["H"], a["Nq"], a["Nk"],
                                  a["d"], a["causal"], 0.125, 2, 0, 0, a["ws"] or None, 1 << 20)
     assert st == code, (args, st)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), 1), (dict(dv=0), 1),
+    (dict(Nq=0), 2), (dict(causal=1), 2),                    # causal needs Nq == Nk
+    (dict(d=96), 3), (dict(i=0, o_t=0, g_t=0), 3),
+    (dict(scale=-1.0), 4),
+    # B*H*Nq rows of 8 bytes beyond the 16 MiB static scratch (2^21 rows)
+    (dict(B=2, H=16, Nq=(1 << 16) + 1, Nk=128), 7), (dict(B=1, H=1, Nq=(1 << 21) + 1, Nk=64), 7),
+])
+def test_bwd_noalloc_error_paths_need_no_gpu(lib, args, code):
+    """attn_bwd_noalloc checks its arguments, and the size of the problem
+    against its static scratch, before any HIP call."""
+    a = dict(q=P, dv=P, B=1, H=1, Nq=64, Nk=80, d=64, causal=0, scale=0.125, i=2, o_t=0, g_t=0)
+    a.update(args)
+    st = binding.attn_bwd_noalloc_raw(a["q"] or None, P, P, P, P, P, P, P, a["dv"] or None, a["B"],
+                                      a["H"], a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                                      a["i"], a["o_t"], a["g_t"])
+    assert st == code, (args, st)
+    assert "static scratch" in binding.status_string(7)
