@@ -10,7 +10,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libattn_fwd.so")
+# ATTN_LIB_PATH selects another build of the same library (e.g. a tile-configuration
+# variant from sweep.py) for the process.
+LIB_PATH = os.environ.get("ATTN_LIB_PATH") or os.path.join(_PKG, "libattn_fwd.so")
 
 # attn_dtype / attn_status values of include/attn.h
 ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2

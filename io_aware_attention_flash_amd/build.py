@@ -144,7 +144,14 @@ def is_stale():
 
 
 def ensure_built(verbose=False):
-    """Build the library when it is missing or stale; return its path."""
+    """Build the library when it is missing or stale; return its path. When
+    ATTN_LIB_PATH names another build (a sweep variant), that one must exist
+    and nothing is built."""
+    other = os.environ.get("ATTN_LIB_PATH")
+    if other:
+        if not os.path.exists(other):
+            raise RuntimeError("ATTN_LIB_PATH=%s does not exist" % other)
+        return other
     if is_stale():
         build(verbose=verbose)
     return LIB

@@ -138,13 +138,45 @@ __device__ __forceinline__ float sum_halves(float x) {
 constexpr int kKStages = 2;
 constexpr int kVStages = 2;
 
-template <int D>
+// Tile shape: waves per workgroup (32 query rows each; 8 -> one workgroup of
+// 256 rows per CU, 4 -> two of 128 rows) and keys per K/V tile, per head
+// dimension. The defaults are the measured choices (io_aware_attention_flash_amd/
+// sweep.py builds and times the alternatives); a build may override them
+// with -D. Combinations whose LDS does not fit, or whose tile copy is not a
+// whole number of instructions, fail to compile.
+// A -D choice of a head dimension's tile applies to every problem; without
+// one the library chooses between two tiles per problem (see pick_launch16).
+#if defined(ATTN_CFG_FWD_WAVES_D64) || defined(ATTN_CFG_FWD_BN_D64)
+#define ATTN_FWD_D64_FORCED 1
+#else
+#define ATTN_FWD_D64_FORCED 0
+#endif
+#if defined(ATTN_CFG_FWD_WAVES_D128) || defined(ATTN_CFG_FWD_BN_D128)
+#define ATTN_FWD_D128_FORCED 1
+#else
+#define ATTN_FWD_D128_FORCED 0
+#endif
+#ifndef ATTN_CFG_FWD_WAVES_D128
+#define ATTN_CFG_FWD_WAVES_D128 8
+#endif
+#ifndef ATTN_CFG_FWD_BN_D128
+#define ATTN_CFG_FWD_BN_D128 64
+#endif
+#ifndef ATTN_CFG_FWD_WAVES_D64
+#define ATTN_CFG_FWD_WAVES_D64 4
+#endif
+#ifndef ATTN_CFG_FWD_BN_D64
+#define ATTN_CFG_FWD_BN_D64 128
+#endif
+
+template <int D_, int WAVES_, int BN_>
 struct Shape16 {
-  static constexpr int WAVES = (D == 128) ? 8 : 4;       // per workgroup
+  static constexpr int D = D_;
+  static constexpr int WAVES = WAVES_;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BLOCK_M = WAVES * 32;             // query rows per workgroup
   static constexpr int WG_PER_CU = 8 / WAVES;            // two waves per SIMD
-  static constexpr int BN = (D == 128) ? 64 : 128;
+  static constexpr int BN = BN_;
   static constexpr int CPR = D / 8;                      // 16-byte chunks per row
   static constexpr int TILE_ELEMS = BN * D;              // one K or V stage
   static constexpr int TILE_BYTES = TILE_ELEMS * 2;
@@ -153,11 +185,11 @@ struct Shape16 {
   static constexpr int Q_INS = BLOCK_M * D * 2 / INS_BYTES;  // DMA instructions for the Q tile
   static constexpr int RING_ELEMS = 4 * TILE_ELEMS;      // K stages 0..1, V stages 0..1
   static_assert(kKStages + kVStages == 4, "ring size");
-  // d=128 (one workgroup per CU) stages O for the epilogue in LDS of its own,
-  // in 128-byte rows, so a workgroup can copy its next tile's first K/V tiles
-  // and Q into the ring while it writes out O; d=64 (two workgroups per CU)
-  // has no room left and stages in the ring, in 256-byte rows.
-  static constexpr bool OWN_STAGE = (D == 128);
+  // A workgroup alone on its CU stages O for the epilogue in LDS of its own,
+  // in 128-byte rows, so it can copy its next tile's first K/V tiles and Q
+  // into the ring while it writes out O; two workgroups per CU have no room
+  // for that and stage in the ring, in 256-byte rows.
+  static constexpr bool OWN_STAGE = WG_PER_CU == 1;
   static constexpr int STAGE_ROWB = OWN_STAGE ? 128 : 256;
   static constexpr int STAGE_ELEMS = OWN_STAGE ? WAVES * 32 * STAGE_ROWB / 2 : 0;
   static constexpr int LDS_ELEMS = RING_ELEMS + BLOCK_M * D + STAGE_ELEMS;
@@ -165,9 +197,21 @@ struct Shape16 {
   static constexpr int NCB = D / 32;                     // 32-column blocks of O^T
   static constexpr int NKC = D / 16;                     // 16-wide QK^T k-chunks
   static constexpr int NT = BN / 16;                     // 16-key PV k-chunks
-  static_assert(DMA_INS * THREADS == BN * CPR, "DMA covers the tile");
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves per workgroup");
+  static_assert(BN == 32 || BN == 64 || BN == 128, "32, 64 or 128 keys per tile");
+  static_assert(DMA_INS >= 1 && DMA_INS * THREADS == BN * CPR, "DMA covers the tile");
   static_assert(DMA_INS * INS_BYTES == TILE_BYTES, "each DMA instruction moves 16 bytes a thread");
+  static_assert((INS_BYTES / (D * 2)) % 16 == 0, "one copy instruction spans whole swizzle periods");
+  static_assert(WG_PER_CU * LDS_ELEMS * 2 <= 160 * 1024, "LDS of the workgroups sharing a CU");
+  // epilogue staging fits (own area, or the ring)
+  static_assert(WAVES * 32 * (OWN_STAGE ? 128 : 256) <= (OWN_STAGE ? STAGE_ELEMS : RING_ELEMS) * 2,
+                "O staging fits");
 };
+
+// The default tile of each head dimension.
+template <int D>
+using Tile16 = Shape16<D, D == 128 ? ATTN_CFG_FWD_WAVES_D128 : ATTN_CFG_FWD_WAVES_D64,
+                       D == 128 ? ATTN_CFG_FWD_BN_D128 : ATTN_CFG_FWD_BN_D64>;
 
 // Compile-time configuration. The defaults are the measured choices; a build
 // may override them with -D (io_aware_attention_flash_amd/sweep.py builds
@@ -180,6 +224,12 @@ struct Shape16 {
 #endif
 #ifndef ATTN_CFG_PREPASS_MIN_N
 #define ATTN_CFG_PREPASS_MIN_N 8192
+#endif
+// Order of the two causal query tiles a workgroup takes: 0 runs the long one
+// first, 1 the short one (which then reads the keys the long one starts
+// with while they are fresh in L2).
+#ifndef ATTN_CFG_CAUSAL_SHORT_FIRST
+#define ATTN_CFG_CAUSAL_SHORT_FIRST 0
 #endif
 
 // Rows of the online softmax are rescaled only when their maximum grows by
@@ -225,9 +275,9 @@ constexpr int kBufferFlags = 0x00020000;
 // one visited), so reads beyond the cut return zeros and touch no memory.
 // Every input is wave-uniform; readfirstlane says so to the compiler, which
 // keeps the words in scalar registers.
-template <int D>
+template <class S>
 __device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N) {
-  constexpr int BN = Shape16<D>::BN;
+  constexpr int BN = S::BN, D = S::D;
   const int keys = t < n_tiles ? min(N - t * BN, BN) : 0;
   const uint16_t *base = keys > 0 ? head + (size_t)t * BN * D : head;
   const uint64_t a = reinterpret_cast<uint64_t>(base);
@@ -258,7 +308,7 @@ __device__ __forceinline__ void dma16_to_lds(u32x4 rsrc, uint32_t lds_byte, uint
 // (the descriptor's range check applies to it, not to an SGPR offset).
 template <int D, bool IS_V>
 __device__ __forceinline__ uint32_t dma_offset(int tid) {
-  constexpr int CPR = Shape16<D>::CPR;
+  constexpr int CPR = D / 8;
   const int row0 = tid / CPR;
   const int swz = IS_V ? swz_v<D>(row0) : swz_k<D>(row0);
   return row0 * D * 2 + (((tid % CPR) ^ swz) << 4);
@@ -345,10 +395,10 @@ __device__ __forceinline__ u32x4 v_frag(const uint16_t *vst, const LaneAddr<D> &
 
 // S^T[kb] = K_kb Q^T for one tile (once per query tile, before the
 // pipelined loop), the K operands read kLookahead steps ahead of their MFMAs.
-template <int D, bool IS_BF16>
+template <class S, bool IS_BF16>
 __device__ __forceinline__ void qk_tile(f32x16 *s, const u32x4 *qf, const uint16_t *kst,
-                                        const LaneAddr<D> &la) {
-  using S = Shape16<D>;
+                                        const LaneAddr<S::D> &la) {
+  constexpr int D = S::D;
   constexpr int NM = S::NKB * S::NKC, LA = kLookahead;
   u32x4 fr[LA + 1];
 #pragma unroll
@@ -387,13 +437,12 @@ __device__ __forceinline__ int score_key(int n0, int kb, int r, int g) {
 // grew by more than kRescaleLog2.
 template <int D>
 __device__ __forceinline__ void rescale(RowState16<D> &st, float m_tile) {
-  using S = Shape16<D>;
   if (__any(m_tile > st.m + kRescaleLog2)) {
     const float m_new = fmaxf(st.m, m_tile);
     const float neg_new = m_new == -INFINITY ? 0.f : -m_new;
     const float alpha = exp2_fast(st.m + neg_new);  // 0 when m was -inf
 #pragma unroll
-    for (int cb = 0; cb < S::NCB; ++cb)
+    for (int cb = 0; cb < D / 32; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.acc[cb][r] *= alpha;
     st.l *= alpha;
@@ -404,10 +453,9 @@ __device__ __forceinline__ void rescale(RowState16<D> &st, float m_tile) {
 
 // Mask, row maximum and rescale for a whole tile of scores at once (the
 // first tile; later tiles do this inside phase 2).
-template <int D, bool CAUSAL, bool MASK>
-__device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0, int N, int qrow,
+template <class S, bool CAUSAL, bool MASK>
+__device__ __forceinline__ void softmax_max(RowState16<S::D> &st, f32x16 *s, int n0, int N, int qrow,
                                             float qk, int g) {
-  using S = Shape16<D>;
   float mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < S::NKB; ++kb)
@@ -416,7 +464,7 @@ __device__ __forceinline__ void softmax_max(RowState16<D> &st, f32x16 *s, int n0
       if constexpr (MASK) s[kb][r] = mask_score<CAUSAL>(s[kb][r], score_key(n0, kb, r, g), N, qrow);
       mx = fmaxf(mx, s[kb][r]);
     }
-  rescale<D>(st, max_halves(mx) * qk);  // qk > 0: the max of the scaled scores
+  rescale<S::D>(st, max_halves(mx) * qk);  // qk > 0: the max of the scaled scores
 }
 
 // Eight bf16 values -> eight fp16 values (round to nearest even; exact for
@@ -429,8 +477,9 @@ __device__ __forceinline__ u32x4 to_f16(u32x4 x) {
 }
 
 // Everything the iterations of one wave touch.
-template <int D>
+template <class S>
 struct Pipe16 {
+  static constexpr int D = S::D;
   uint16_t *lds;  // K stages 0..1, then V stages 0..1 (tile t in stage t % 2)
   const uint16_t *Kh, *Vh;
   LaneAddr<D> la;
@@ -438,35 +487,34 @@ struct Pipe16 {
   uint32_t lds_wave;  // LDS byte address of the buffer plus 1024 * wave (uniform)
   // Source offsets of this thread's 16 bytes in copy instruction c (kept in
   // registers: the descriptor's range check applies to them).
-  uint32_t k_dma[Shape16<D>::DMA_INS], v_dma[Shape16<D>::DMA_INS];
+  uint32_t k_dma[S::DMA_INS], v_dma[S::DMA_INS];
   float qk;
 
   __device__ __forceinline__ uint16_t *kstage(int par) const {
-    return lds + par * Shape16<D>::TILE_ELEMS;
+    return lds + par * S::TILE_ELEMS;
   }
   __device__ __forceinline__ uint16_t *vstage(int par) const {
-    return lds + (kKStages + par) * Shape16<D>::TILE_ELEMS;
+    return lds + (kKStages + par) * S::TILE_ELEMS;
   }
   // The query tile (BLOCK_M rows, K's layout) after the rings.
-  __device__ __forceinline__ uint16_t *qstage() const { return lds + Shape16<D>::RING_ELEMS; }
+  __device__ __forceinline__ uint16_t *qstage() const { return lds + S::RING_ELEMS; }
   // Tile copies. Iteration j reads K_{j+1} and V_j. Its first steps issue
   // V_{j+1}, then K_{j+2}, into the stages V_{j-1} and K_j left (free since
   // the barrier that ended iteration j-1); a late step waits for V_{j+1}
   // and converts it (bf16); the iteration ends by waiting for K_{j+2}.
-  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<D>(Kh, t, n_tiles, N); }
-  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<D>(Vh, t, n_tiles, N); }
+  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<S>(Kh, t, n_tiles, N); }
+  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<S>(Vh, t, n_tiles, N); }
   // Instruction c of the copy of K_t / V_t (descriptor r).
   __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
-    constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (t & 1) * TB + c * Shape16<D>::INS_BYTES, k_dma[c]);
+    constexpr int TB = S::TILE_BYTES;
+    dma16_to_lds(r, lds_wave + (t & 1) * TB + c * S::INS_BYTES, k_dma[c]);
   }
   __device__ __forceinline__ void copy_v(u32x4 r, int t, int c) const {
-    constexpr int TB = Shape16<D>::TILE_BYTES;
-    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * Shape16<D>::INS_BYTES, v_dma[c]);
+    constexpr int TB = S::TILE_BYTES;
+    dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * S::INS_BYTES, v_dma[c]);
   }
   // Copy of the workgroup's query tile (rows m0 ..; rows past N read as 0).
   __device__ __forceinline__ void issue_q(const uint16_t *Qh, int m0) const {
-    using S = Shape16<D>;
     const int rows = min(N - m0, S::BLOCK_M);
     const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * D);
     const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
@@ -479,24 +527,24 @@ struct Pipe16 {
   __device__ __forceinline__ void issue_k(int t) const {
     const u32x4 r = k_rsrc(t);
 #pragma unroll
-    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) copy_k(r, t, c);
+    for (int c = 0; c < S::DMA_INS; ++c) copy_k(r, t, c);
   }
   __device__ __forceinline__ void issue_v(int t) const {
     const u32x4 r = v_rsrc(t);
 #pragma unroll
-    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) copy_v(r, t, c);
+    for (int c = 0; c < S::DMA_INS; ++c) copy_v(r, t, c);
   }
   // 16-byte slot c of the ones this thread's own copy of V_t wrote: after
   // the copy has landed (this wave's vmcnt wait), the thread converts them
   // from bf16 to fp16 in place.
   __device__ __forceinline__ u32x4 *v_slot(int t, int c) const {
-    return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * (Shape16<D>::INS_BYTES / 2) + tid * 8);
+    return reinterpret_cast<u32x4 *>(vstage(t & 1) + c * (S::INS_BYTES / 2) + tid * 8);
   }
   template <bool CONV_V>
   __device__ __forceinline__ void convert_v(int t) const {
     if (!CONV_V || t >= n_tiles) return;
 #pragma unroll
-    for (int c = 0; c < Shape16<D>::DMA_INS; ++c) *v_slot(t, c) = to_f16(*v_slot(t, c));
+    for (int c = 0; c < S::DMA_INS; ++c) *v_slot(t, c) = to_f16(*v_slot(t, c));
   }
 };
 
@@ -509,25 +557,37 @@ struct Pipe16 {
 // taking S_j's first blocks early lets the later blocks of S_{j+1} reuse
 // their registers (five blocks live at a time for d=128, six for d=64, not
 // eight), while the vector work still spreads over most of the MFMAs.
-template <int D>
+template <class S>
 struct PairPlan {
-  using S = Shape16<D>;
+  static constexpr int D = S::D;
   static constexpr int NM1 = S::NKB * S::NKC;
   static constexpr int NM2 = S::NT * S::NCB;
   static constexpr int NP = S::NT * 4;
-  static constexpr int F = D == 128 ? 8 : 16;
-  static constexpr int FS = D == 128 ? 8 : 12;
   static constexpr int deadline(int p) { return NM1 + (p >> 2) * S::NCB - 1; }
   static constexpr int LAST = deadline(NP - 1) - 2;
-  static constexpr int start(int p) {
-    return p < F ? p * FS / F : FS + (p - F) * (LAST - FS) / (NP - 1 - F);
+  static constexpr int start_fs(int p, int f, int fs) {
+    return p < f ? p * fs / f : fs + (p - f) * (LAST - fs) / (NP - 1 - f);
   }
-  static constexpr bool valid() {
+  static constexpr bool valid_fs(int f, int fs) {
     for (int p = 0; p < NP; ++p)
-      if (start(p) + 2 > deadline(p) || (p > 0 && start(p) < start(p - 1))) return false;
-    return start(NP - 1) == LAST;
+      if (start_fs(p, f, fs) + 2 > deadline(p) || (p > 0 && start_fs(p, f, fs) < start_fs(p - 1, f, fs)))
+        return false;
+    return start_fs(NP - 1, f, fs) == LAST;
   }
-  static_assert(valid(), "every pair is packed before its P.V step");
+  // The measured spread for the default tiles (d=128: 64 keys, d=64: 128);
+  // for other tiles the widest valid one, front pairs first.
+  static constexpr int pick(bool want_fs) {
+    if (D == 128 && S::BN == 64 && valid_fs(8, 8)) return 8;
+    if (D == 64 && S::BN == 128 && valid_fs(16, 12)) return want_fs ? 12 : 16;
+    for (int f = NP / 2; f >= 1; --f)
+      for (int fs = f; fs >= 1; --fs)
+        if (valid_fs(f, fs)) return want_fs ? fs : f;
+    return 0;
+  }
+  static constexpr int F = pick(false);
+  static constexpr int FS = pick(true);
+  static constexpr int start(int p) { return start_fs(p, F, FS); }
+  static_assert(F > 0 && valid_fs(F, FS), "every pair is packed before its P.V step");
   // First pair starting at step i or later, and the most pairs one step starts.
   static constexpr int first_at(int i) {
     int p = 0;
@@ -557,12 +617,11 @@ struct PairPlan {
 // slot per two steps (load, then convert and store). VPAR is j's parity
 // when known at compile time (-1 otherwise), which makes the V stage
 // addresses constants.
-template <int D, bool IS_BF16, bool CONV_V, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
-__device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
-                                          int j, f32x16 (&s)[Shape16<D>::NKB],
-                                          f32x16 (&s_next)[Shape16<D>::NKB]) {
-  using S = Shape16<D>;
-  using PP = PairPlan<D>;
+template <class S, bool IS_BF16, bool CONV_V, bool CAUSAL, bool MASK_NEXT, bool NEXT, int VPAR>
+__device__ __forceinline__ void iteration(const Pipe16<S> &pp, RowState16<S::D> &st, const u32x4 *qf,
+                                          int j, f32x16 (&s)[S::NKB], f32x16 (&s_next)[S::NKB]) {
+  constexpr int D = S::D;
+  using PP = PairPlan<S>;
   constexpr int LA = kLookahead;
   constexpr int NM1 = PP::NM1, NM2 = PP::NM2, NP = PP::NP;
   constexpr int NS = NM1 + NM2;
@@ -667,11 +726,9 @@ __device__ __forceinline__ void iteration(const Pipe16<D> &pp, RowState16<D> &st
 // All iterations of one wave. nw: key tiles this wave visits, nfw: leading
 // tiles it needs no mask for; the workgroup runs pp.n_tiles iterations, each
 // ending with the copies' wait, the bf16 conversion and a barrier.
-template <int D, bool IS_BF16, bool CONV_V, bool CAUSAL>
-__device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st, const u32x4 *qf,
-                                         f32x16 (&sa)[Shape16<D>::NKB],
-                                         f32x16 (&sb)[Shape16<D>::NKB], int nw, int nfw) {
-  using S = Shape16<D>;
+template <class S, bool IS_BF16, bool CONV_V, bool CAUSAL>
+__device__ __forceinline__ void run_wave(const Pipe16<S> &pp, RowState16<S::D> &st, const u32x4 *qf,
+                                         f32x16 (&sa)[S::NKB], f32x16 (&sb)[S::NKB], int nw, int nfw) {
   const int n = pp.n_tiles;
 #define ITER(work)                                               \
   do {                                                           \
@@ -682,21 +739,21 @@ __device__ __forceinline__ void run_wave(const Pipe16<D> &pp, RowState16<D> &st,
   int j = 0;
   const int n_a = max(min(nfw, nw) - 1, 0);  // tiles j < n_a have an unmasked successor
   for (; j + 2 <= n_a; j += 2) {
-    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
-    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
+    ITER((iteration<S, IS_BF16, CONV_V, CAUSAL, false, true, 0>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<S, IS_BF16, CONV_V, CAUSAL, false, true, 1>(pp, st, qf, j + 1, sb, sa)));
   }
   if (j < n_a) {  // odd count of unmasked successors
-    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<S, IS_BF16, CONV_V, CAUSAL, false, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
     ++j;
   }
   for (; j < nw - 1; ++j) {
-    ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
+    ITER((iteration<S, IS_BF16, CONV_V, CAUSAL, true, true, -1>(pp, st, qf, j, sa, sb)));
 #pragma unroll
     for (int kb = 0; kb < S::NKB; ++kb) sa[kb] = sb[kb];
   }
-  ITER((iteration<D, IS_BF16, CONV_V, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
+  ITER((iteration<S, IS_BF16, CONV_V, CAUSAL, false, false, -1>(pp, st, qf, j, sa, sb)));
   // Tiles past this wave's rows: the same copies, conversion and waits.
   for (++j; j < n; ++j) {
     pp.issue_v(j + 1);
@@ -819,10 +876,10 @@ struct OutStage {
 // prefetched: the previous tile of this workgroup (same head) already copied
 // this tile's Q, V_0, K_0 and K_1. next_qt >= 0: copy that tile's ones once
 // this tile's loop is done.
-template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
+template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
 __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int bh, int qt,
                                           bool prefetched, int next_qt) {
-  using S = Shape16<D>;
+  constexpr int D = S::D;
   constexpr int BN = S::BN;
   constexpr int NCB = S::NCB;
   constexpr int NKC = S::NKC;
@@ -840,7 +897,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   const size_t head = (size_t)bh * (size_t)N * D;
   const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + head;
 
-  Pipe16<D> pp;
+  Pipe16<S> pp;
   pp.lds = lds;
   pp.Kh = static_cast<const uint16_t *>(p.k) + head;
   pp.Vh = static_cast<const uint16_t *>(p.v) + head;
@@ -899,15 +956,15 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) qf[kc] = k_frag<D>(pp.qstage(), pp.la, wave, kc);
   f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
-  qk_tile<D, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
+  qk_tile<S, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
   if (nfw == 0)
-    softmax_max<D, CAUSAL, true>(st, sa, 0, N, pp.qrow, pp.qk, g);
+    softmax_max<S, CAUSAL, true>(st, sa, 0, N, pp.qrow, pp.qk, g);
   else
-    softmax_max<D, CAUSAL, false>(st, sa, 0, N, pp.qrow, pp.qk, g);
+    softmax_max<S, CAUSAL, false>(st, sa, 0, N, pp.qrow, pp.qk, g);
   wait_vmcnt<0>();  // K_1
   lds_barrier();
 
-  run_wave<D, IS_BF16, CONV_V, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
+  run_wave<S, IS_BF16, CONV_V, CAUSAL>(pp, st, qf, sa, sb, nw, nfw);
 
   // Copies issued for tiles past the end (empty byte ranges) retire before
   // the workgroup's LDS can be handed to another one.
@@ -994,9 +1051,8 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 // start together, so each head's K/V stream through that XCD's L2 about once
 // rather than once per wave of workgroups. Otherwise ids run item-major,
 // head-minor.
-template <int D, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
-__global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void attn_fwd_16(FwdParams p) {
-  using S = Shape16<D>;
+template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
+__global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
   const int w = blockIdx.x;
   int t, bh;
@@ -1011,16 +1067,18 @@ __global__ __launch_bounds__(Shape16<D>::THREADS, Shape16<D>::WG_PER_CU) void at
     bh = w - t * p.BH;
   }
   if (!CAUSAL) {
-    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
     return;
   }
-  const int qa = p.nq - 1 - t, qb = t;
-  const int n_items = qb < qa ? 2 : 1;
+  const int q_long = p.nq - 1 - t, q_short = t;
+  const int n_items = q_short < q_long ? 2 : 1;
+  const int qa = ATTN_CFG_CAUSAL_SHORT_FIRST && n_items == 2 ? q_short : q_long;
+  const int qb = ATTN_CFG_CAUSAL_SHORT_FIRST && n_items == 2 ? q_long : q_short;
 #pragma unroll 1
   for (int k = 0; k < n_items; ++k) {
     // The second tile's copies reuse the LDS the first one's epilogue read.
     if (k > 0) lds_barrier();
-    attn_tile<D, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb,
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb,
                                                    S::OWN_STAGE && k > 0,
                                                    k + 1 < n_items ? qb : -1);
   }
@@ -1170,21 +1228,83 @@ constexpr int64_t kPrepassMinN = ATTN_CFG_PREPASS_MIN_N;
 // --------------------------------------------------------------------------
 typedef void (*KernelFn)(FwdParams);
 
-template <int D, bool IS_BF16, bool CAUSAL>
+// A bf16/fp16 kernel and its launch shape.
+struct Launch16 {
+  KernelFn fn;
+  int block_m;       // query rows per workgroup
+  unsigned threads;  // threads per workgroup
+};
+
+template <class S, bool IS_BF16, bool CAUSAL>
 KernelFn pick16(bool out_f32, bool conv_v) {
   if (IS_BF16 && conv_v)
-    return out_f32 ? attn_fwd_16<D, IS_BF16, CAUSAL, true, IS_BF16>
-                   : attn_fwd_16<D, IS_BF16, CAUSAL, false, IS_BF16>;
-  return out_f32 ? attn_fwd_16<D, IS_BF16, CAUSAL, true, false>
-                 : attn_fwd_16<D, IS_BF16, CAUSAL, false, false>;
+    return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, IS_BF16>
+                   : attn_fwd_16<S, IS_BF16, CAUSAL, false, IS_BF16>;
+  return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, false>
+                 : attn_fwd_16<S, IS_BF16, CAUSAL, false, false>;
 }
 
-template <int D>
-KernelFn pick_d(attn_dtype in, bool out_f32, bool causal, bool conv_v) {
-  if (in == ATTN_F32) return causal ? attn_fwd_f32<D, true> : attn_fwd_f32<D, false>;
+template <class S>
+Launch16 launch16(attn_dtype in, bool out_f32, bool causal, bool conv_v) {
+  KernelFn fn;
   if (in == ATTN_BF16)
-    return causal ? pick16<D, true, true>(out_f32, conv_v) : pick16<D, true, false>(out_f32, conv_v);
-  return causal ? pick16<D, false, true>(out_f32, false) : pick16<D, false, false>(out_f32, false);
+    fn = causal ? pick16<S, true, true>(out_f32, conv_v) : pick16<S, true, false>(out_f32, conv_v);
+  else
+    fn = causal ? pick16<S, false, true>(out_f32, false) : pick16<S, false, false>(out_f32, false);
+  return Launch16{fn, S::BLOCK_M, (unsigned)S::THREADS};
+}
+
+// The tile of a problem. The pages key their autotuning on the sequence
+// length, the head dimension and the mask; here two compiled tiles per head
+// dimension compete: 8 waves (one 256-row workgroup per CU; d=128: 64-key
+// tiles, d=64: 128-key) and 4 waves (two 128-row workgroups per CU; d=128:
+// 32-key tiles, d=64: 64-key). Measured at full occupancy, the 8-wave tile
+// is faster per unit of work (5% at d=64, 10% at d=128), but the grid runs
+// in whole rounds of workgroups: a last round that is only partly filled
+// leaves CUs idle for a whole workgroup's time, and with 4-wave tiles a
+// last round of at most one workgroup per CU runs each alone on its CU,
+// faster (taken as 0.6 of a round). Each tile's cost is its number of
+// rounds so weighted, times its per-unit cost; the cheaper one is taken
+// (io_aware_attention_flash_amd/sweep.py measured every tile on workloads
+// with whole and partial last rounds; this rule picks the faster tile on
+// each of them).
+constexpr int kCUs = 256;
+
+double tile_cost(int64_t units, int wg_per_cu, double unit_cost) {
+  const double rounds = (double)units / (double)(kCUs * wg_per_cu);
+  const double full = (double)(int64_t)rounds, frac = rounds - full;
+  double last = 0.0;
+  if (frac > 0.0) last = wg_per_cu == 2 && frac <= 0.5 ? 0.6 : 1.0;
+  return (full + last) * unit_cost;
+}
+
+// Whether the 8-wave tile is the cheaper one for B*H heads of N rows.
+bool pick_wide(int64_t BH, int64_t N, bool causal, double narrow_unit_cost) {
+  const int64_t nq8 = (N + 255) / 256, nq4 = (N + 127) / 128;
+  const int64_t u8 = (causal ? (nq8 + 1) / 2 : nq8) * BH;
+  const int64_t u4 = (causal ? (nq4 + 1) / 2 : nq4) * BH;
+  return tile_cost(u8, 1, 1.0) <= tile_cost(u4, 2, narrow_unit_cost);
+}
+
+Launch16 pick_launch16(int64_t d, int64_t BH, int64_t N, attn_dtype in, bool out_f32,
+                       bool causal, bool conv_v) {
+  if (d == 128) {
+#if ATTN_FWD_D128_FORCED
+    (void)BH;
+    return launch16<Tile16<128>>(in, out_f32, causal, conv_v);
+#else
+    if (pick_wide(BH, N, causal, 1.10))
+      return launch16<Shape16<128, 8, 64>>(in, out_f32, causal, conv_v);
+    return launch16<Shape16<128, 4, 32>>(in, out_f32, causal, conv_v);
+#endif
+  }
+#if ATTN_FWD_D64_FORCED
+  return launch16<Tile16<64>>(in, out_f32, causal, conv_v);
+#else
+  if (pick_wide(BH, N, causal, 1.05))
+    return launch16<Shape16<64, 8, 128>>(in, out_f32, causal, conv_v);
+  return launch16<Shape16<64, 4, 64>>(in, out_f32, causal, conv_v);
+#endif
 }
 
 // Bytes of the fp16 copy of V the first pass writes, or 0 when the problem
@@ -1240,10 +1360,19 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   if (in_dtype != ATTN_F32 && out_dtype != in_dtype && out_dtype != ATTN_F32)
     return ATTN_ERR_UNSUPPORTED;
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
-  // Query rows per workgroup and threads per workgroup of the chosen kernel.
+  // The first pass runs when the problem takes it and the workspace can hold
+  // its output (16-byte aligned); otherwise the kernel converts V in LDS.
+  // Both give the same bits.
+  const size_t need = prepass_bytes(B, H, N, d, in_dtype);
+  const bool prepass = need > 0 && workspace != nullptr && workspace_bytes >= need &&
+                       (reinterpret_cast<uintptr_t>(workspace) & 15) == 0;
+  const bool out_f32 = out_dtype == ATTN_F32;
+  // The kernel, and its query rows and threads per workgroup.
   const bool f32_path = in_dtype == ATTN_F32;
-  const int64_t block_m = f32_path ? kBlockM : d == 64 ? Shape16<64>::BLOCK_M : Shape16<128>::BLOCK_M;
-  const unsigned threads = f32_path ? kThreads : d == 64 ? Shape16<64>::THREADS : Shape16<128>::THREADS;
+  Launch16 l16 = {nullptr, 0, 0};
+  if (!f32_path) l16 = pick_launch16(d, B * H, N, in_dtype, out_f32, causal != 0, !prepass);
+  const int64_t block_m = f32_path ? kBlockM : l16.block_m;
+  const unsigned threads = f32_path ? kThreads : l16.threads;
   const int64_t nq = (N + block_m - 1) / block_m;
   // Causal bf16/fp16 workgroups take two query tiles each (long + short).
   const int64_t grid = (causal && !f32_path ? (nq + 1) / 2 : nq) * B * H;
@@ -1264,15 +1393,10 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   double qk = (double)scale * 1.4426950408889634;
   p.qk = qk < (double)FLT_MIN ? FLT_MIN : (float)qk;
 
-  // The first pass runs when the problem takes it and the workspace can hold
-  // its output (16-byte aligned); otherwise the kernel converts V in LDS.
-  // Both give the same bits.
-  const size_t need = prepass_bytes(B, H, N, d, in_dtype);
-  const bool prepass = need > 0 && workspace != nullptr && workspace_bytes >= need &&
-                       (reinterpret_cast<uintptr_t>(workspace) & 15) == 0;
-  const bool out_f32 = out_dtype == ATTN_F32;
-  KernelFn fn = d == 64 ? pick_d<64>(in_dtype, out_f32, causal != 0, !prepass)
-                        : pick_d<128>(in_dtype, out_f32, causal != 0, !prepass);
+  KernelFn fn = l16.fn;
+  if (f32_path)
+    fn = d == 64 ? (causal ? attn_fwd_f32<64, true> : attn_fwd_f32<64, false>)
+                 : (causal ? attn_fwd_f32<128, true> : attn_fwd_f32<128, false>);
   hipStream_t st = (hipStream_t)stream;
   hipError_t err = hipSuccess;
   if (prepass) {

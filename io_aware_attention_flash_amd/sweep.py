@@ -32,6 +32,30 @@ SWEEP_DIR = os.path.join(hipbuild.ROOT, "build", "sweep")
 # or a label when the shipped value depends on the head dimension), the pass
 # that exercises it and the workloads it is timed on.
 KNOBS = {
+    "fwd_tile_d128": dict(macro=("ATTN_CFG_FWD_WAVES_D128", "ATTN_CFG_FWD_BN_D128"),
+                          values=["dispatch", "8x64", "8x32", "4x32"], pass_="fwd",
+                          workloads=["b2h32_n4096_d128_bf16_causal",
+                                     "b1h16_n16384_d128_bf16_sigma3_causal",
+                                     "b4h16_n1024_d128_bf16", "b8h12_n3000_d128_bf16",
+                                     "b1h8_n2048_d128_bf16_causal"],
+                          what="forward tile at d=128: waves per workgroup (32 query rows "
+                               "each) x keys per K/V tile (shipped: chosen per problem between "
+                               "8x64 and 4x32 by a round-count cost model)"),
+    "fwd_tile_d64": dict(macro=("ATTN_CFG_FWD_WAVES_D64", "ATTN_CFG_FWD_BN_D64"),
+                         values=["dispatch", "4x128", "4x64", "8x128", "8x64"], pass_="fwd",
+                         workloads=["b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16",
+                                    "b4h16_n2048_d64_bf16", "b2h16_n8192_d64_bf16",
+                                    "b2h16_n4096_d64_bf16_causal", "b1h16_n16384_d64_bf16_causal",
+                                    "b8h16_n512_d64_bf16_causal"],
+                         what="forward tile at d=64: waves per workgroup x keys per K/V tile "
+                              "(shipped: chosen per problem between 8x128 and 4x64 by a "
+                              "round-count cost model)"),
+    "fwd_causal_short_first": dict(macro="ATTN_CFG_CAUSAL_SHORT_FIRST", values=[0, 1],
+                                   pass_="fwd",
+                                   workloads=["b2h32_n4096_d128_bf16_causal",
+                                              "b1h16_n16384_d128_bf16_sigma3_causal"],
+                                   what="causal workgroups run their short query tile first "
+                                        "(1) or their long one (0)"),
     "fwd_lookahead": dict(macro="ATTN_CFG_LOOKAHEAD", values=[3, 2, 4], pass_="fwd",
                           workloads=["b2h32_n4096_d128_bf16_causal",
                                      "b1h16_n16384_d128_bf16_sigma3_causal"],
@@ -68,7 +92,18 @@ KNOBS = {
 
 
 def variant_name(knob, value):
-    return "default" if value == KNOBS[knob]["values"][0] else "%s_%d" % (knob, value)
+    return "default" if value == KNOBS[knob]["values"][0] else "%s_%s" % (knob, value)
+
+
+def variant_defs(knob, value):
+    """-D flags of one value: a number for a one-macro knob, or "AxB" for a
+    knob over a pair of macros."""
+    macro = KNOBS[knob]["macro"]
+    if isinstance(value, str) and "x" not in value:
+        return []  # the library's own per-problem choice
+    if isinstance(macro, tuple):
+        return ["-D%s=%s" % (m, x) for m, x in zip(macro, str(value).split("x"))]
+    return ["-D%s=%d" % (macro, value)]
 
 
 def _alternatives(knob):
@@ -94,7 +129,7 @@ def build_all(jobs=4, knobs=None):
         if knobs and knob not in knobs:
             continue
         for v in _alternatives(knob):
-            todo.append((variant_name(knob, v), ["-D%s=%d" % (k["macro"], v)]))
+            todo.append((variant_name(knob, v), variant_defs(knob, v)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for msg in ex.map(lambda t: _build_one(*t), todo):
             print(msg, flush=True)
@@ -106,6 +141,22 @@ def _workload(name):
         return WORKLOADS[name]
     if name == "b1h32_n8192_d128_bf16_causal":
         return Workload(name, 1, 32, 8192, 128, "bf16", True)
+    if name == "b4h16_n1024_d128_bf16":
+        return Workload(name, 4, 16, 1024, 128, "bf16", False)
+    if name == "b2h16_n4096_d64_bf16_causal":
+        return Workload(name, 2, 16, 4096, 64, "bf16", True)
+    if name == "b8h12_n3000_d128_bf16":
+        return Workload(name, 8, 12, 3000, 128, "bf16", False)
+    if name == "b1h8_n2048_d128_bf16_causal":
+        return Workload(name, 1, 8, 2048, 128, "bf16", True)
+    if name == "b4h16_n2048_d64_bf16":
+        return Workload(name, 4, 16, 2048, 64, "bf16", False)
+    if name == "b2h16_n8192_d64_bf16":
+        return Workload(name, 2, 16, 8192, 64, "bf16", False)
+    if name == "b1h16_n16384_d64_bf16_causal":
+        return Workload(name, 1, 16, 16384, 64, "bf16", True)
+    if name == "b8h16_n512_d64_bf16_causal":
+        return Workload(name, 8, 16, 512, 64, "bf16", True)
     raise KeyError(name)
 
 
@@ -219,8 +270,9 @@ def markdown(results):
     lines = ["| knob (macro) | value | pass | workload | µs | vs shipped | max abs diff vs shipped |",
              "|---|---|---|---|---|---|---|"]
     for r in results:
+        macro = r["macro"] if isinstance(r["macro"], str) else " x ".join(r["macro"])
         lines.append("| %s (`%s`) | %s%s | %s | %s | %.1f | %+.2f%% | %.1e |" % (
-            r["knob"], r["macro"], r["value"], " (shipped)" if r["shipped"] else "", r["pass_"],
+            r["knob"], macro, r["value"], " (shipped)" if r["shipped"] else "", r["pass_"],
             r["workload"], r["us"], 100 * r["rel"], r["max_abs_diff_vs_shipped"]))
     return "\n".join(lines)
 

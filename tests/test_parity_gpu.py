@@ -74,7 +74,7 @@ SMALL_CASES = [
     (1, 2, 517, 128, "bf16", True, 3.0),
     (1, 2, 640, 64, "f16", True, 1.0),
     (1, 1, 1000, 128, "bf16", False, 3.0),
-    # tile edges: d=128 uses 64-key tiles, d=64 128-key tiles
+    # key-tile edges (d=128: 32 or 64 keys per tile, d=64: 64 or 128)
     (1, 2, 64, 128, "f16", False, 1.0),
     (1, 2, 128, 64, "bf16", True, 1.0),
     (1, 2, 129, 64, "bf16", False, 1.0),
@@ -82,12 +82,19 @@ SMALL_CASES = [
     (1, 1, 192, 128, "f16", True, 1.0),
     (1, 1, 385, 64, "f16", True, 2.0),
     (3, 5, 97, 128, "bf16", True, 1.0),
-    # d=128 workgroups hold 256 query rows, d=64 ones 128
+    # query-tile edges (128 or 256 rows per workgroup)
     (1, 1, 255, 128, "bf16", True, 1.0),
     (1, 1, 256, 128, "f16", True, 1.0),
     (1, 2, 257, 128, "bf16", False, 1.0),
     (1, 1, 511, 128, "f16", False, 1.0),
     (2, 1, 513, 128, "bf16", True, 2.0),
+    # enough heads that the 256-row tiles fill whole rounds of workgroups, so
+    # the library takes them (d=128: 64-key tiles, d=64: 128-key), with
+    # ragged last query and key tiles; the cases above take the 128-row ones
+    (4, 16, 2000, 128, "bf16", True, 1.0),
+    (8, 32, 1000, 128, "f16", False, 1.0),
+    (8, 16, 1000, 64, "bf16", True, 2.0),
+    (4, 16, 1000, 64, "f16", False, 1.0),
     # B*H a multiple of 8: workgroup ids run head-major within each XCD
     (2, 8, 700, 128, "bf16", True, 1.0),
     (1, 16, 777, 128, "f16", False, 1.0),
