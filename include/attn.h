@@ -140,7 +140,8 @@ attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, fl
 /*
  * attn_bwd_workspace_bytes -- bytes of device workspace attn_bwd needs:
  * 8 bytes per query row (B*H*N rows), rounded up to 256; 0 for an invalid
- * problem (sizes out of range or d not 64 or 128). No HIP call is made.
+ * problem (sizes out of range, or d not a multiple of 8 in [8, 128]). No HIP
+ * call is made.
  */
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
 
@@ -164,13 +165,19 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
  * atomics: the result is deterministic).
  *
  * q, k, v, dout : device, [B][H][N][d] contiguous, element type in_dtype
- *                 (BF16 or F16).
+ *                 (BF16, F16 or F32).
  * o             : device, [B][H][N][d] contiguous, element type o_dtype
- *                 (in_dtype or F32): the forward's output.
+ *                 (in_dtype or F32; F32 for F32 inputs): the forward's output.
  * lse           : device, [B][H][N] contiguous fp32: the forward's LSE.
  * dq, dk, dv    : device, [B][H][N][d] contiguous, element type grad_dtype
- *                 (in_dtype or F32); written.
- * B, H, N, d, causal, scale : as for attn_fwd (the forward's values).
+ *                 (in_dtype or F32; F32 for F32 inputs); written.
+ * B, H, N, causal, scale : as for attn_fwd (the forward's values).
+ * d             : head dimension, a multiple of 8 in [8, 128]. The kernels
+ *                 work at 64 or 128 columns; the columns past d read as
+ *                 zeros (the padding note of "4.4 Writing GPU Kernels with
+ *                 Triton", section "Sizing the attention kernel": a zero
+ *                 column adds nothing to any score or to D, and its
+ *                 gradients are zero and never stored).
  * workspace     : device, at least attn_bwd_workspace_bytes() bytes, 16-byte
  *                 aligned; caller-owned, contents on entry irrelevant and
  *                 unspecified afterwards. It must not be used by other work
@@ -180,8 +187,8 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
  * Precision: Q K^T, dO V^T and the three gradient products run on the
  * matrix cores in the input type with fp32 accumulation; P and dS are
  * rounded to the input type for the products that take them, and every
- * other quantity is fp32. fp32 inputs are not supported by the backward
- * (ATTN_ERR_UNSUPPORTED).
+ * other quantity is fp32. fp32 inputs run in fp32 throughout
+ * (v_mfma_f32_32x32x2_f32), the page's check of the backward in fp32.
  * Limits and errors: those of attn_fwd, plus ATTN_ERR_WORKSPACE when the
  * workspace is NULL, too small or misaligned. Every argument is validated
  * before any HIP call. Outputs must not alias inputs (not checked).
@@ -206,6 +213,30 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
                         float scale, attn_dtype in_dtype, attn_dtype o_dtype,
                         attn_dtype grad_dtype, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/*
+ * attn_bwd_strided -- attn_bwd_qk for strided tensors.
+ *
+ * Every tensor argument but lse comes with the element strides of its
+ * (batch, head, row) dimensions, or NULL for a contiguous [B][H][n][d]
+ * tensor; the column stride is 1. The kernels take the strides as they are
+ * (no copies): the [B, N, H, d] layout of a fused projection, seen as
+ * [B, H, N, d], needs nothing else. lse is [B][H][Nq] contiguous fp32; the
+ * workspace is attn_bwd_qk's. Each view must have non-negative strides, a
+ * row stride >= d, rows starting 16-byte aligned (base and every stride a
+ * multiple of 16 bytes), every offset below 2^47 elements, and 128 rows
+ * spanning less than 2^31 bytes; otherwise ATTN_ERR_UNSUPPORTED. Every
+ * other argument, check, error and result is that of attn_bwd_qk.
+ */
+attn_status attn_bwd_strided(const void *q, const int64_t *q_strides, const void *k,
+                             const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                             const void *o, const int64_t *o_strides, const float *lse,
+                             const void *dout, const int64_t *dout_strides, void *dq,
+                             const int64_t *dq_strides, void *dk, const int64_t *dk_strides,
+                             void *dv, const int64_t *dv_strides, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                             attn_dtype in_dtype, attn_dtype o_dtype, attn_dtype grad_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * attn_bwd_noalloc -- attn_bwd_qk without a workspace argument and without

@@ -19,7 +19,7 @@ ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_UNSUPPORTED",
           4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_HIP", 6: "ATTN_ERR_WORKSPACE", 7: "ATTN_ERR_CAPACITY"}
 EXPORTS = ("attn_fwd", "attn_fwd_ws", "attn_fwd_workspace_bytes", "attn_fwd_strided", "attn_bwd",
-           "attn_bwd_qk", "attn_bwd_noalloc",
+           "attn_bwd_qk", "attn_bwd_noalloc", "attn_bwd_strided",
            "attn_bwd_workspace_bytes", "attn_row_softmax", "attn_status_string", "attn_abi_version",
            "attn_last_hip_error")
 
@@ -70,6 +70,11 @@ def load_library(path=LIB_PATH):
     lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
                                      ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_int, vp]
+    lib.attn_bwd_strided.restype = ctypes.c_int
+    lib.attn_bwd_strided.argtypes = [vp, i64p, vp, i64p, vp, i64p, vp, i64p, vp, vp, i64p, vp, i64p,
+                                     vp, i64p, vp, i64p, i64, i64, i64, i64, i64, ctypes.c_int,
+                                     ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                     ctypes.c_size_t, vp]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -274,38 +279,50 @@ def bwd_workspace_bytes(B, H, N, d):
     return int(load_library().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d)))
 
 
+def attn_bwd_strided_raw(q_ptr, q_st, k_ptr, k_st, v_ptr, v_st, o_ptr, o_st, lse_ptr, do_ptr,
+                         do_st, dq_ptr, dq_st, dk_ptr, dk_st, dv_ptr, dv_st, B, H, Nq, Nk, d,
+                         causal, scale, in_dtype, o_dtype, grad_dtype, ws_ptr, ws_bytes,
+                         stream=None):
+    """Direct call of attn_bwd_strided; *_st are (b, h, row) element strides
+    or None (contiguous). Returns the status."""
+    return load_library().attn_bwd_strided(
+        q_ptr, _strides(q_st), k_ptr, _strides(k_st), v_ptr, _strides(v_st), o_ptr, _strides(o_st),
+        lse_ptr, do_ptr, _strides(do_st), dq_ptr, _strides(dq_st), dk_ptr, _strides(dk_st), dv_ptr,
+        _strides(dv_st), int(B), int(H), int(Nq), int(Nk), int(d), int(bool(causal)),
+        float(scale), int(in_dtype), int(o_dtype), int(grad_dtype), ws_ptr, int(ws_bytes), stream)
+
+
 def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, workspace=None,
              grads=None):
     """Attention backward on the current HIP stream: (dq, dk, dv) for the
     upstream gradient dout, given the forward's inputs, its output o (input
     dtype or float32) and its lse. q, o and dout are [B, H, Nq, d]; k and v
-    [B, H, Nk, d] (Nk may differ from Nq when not causal). grad_dtype
-    defaults to the input dtype (torch.float32 is also accepted). The
-    workspace (a uint8 tensor of at least bwd_workspace_bytes(B, H, Nq, d)
-    bytes) is taken from torch's allocator when not given. Preallocated
-    (dq, dk, dv) may be passed as `grads`.
-
-    The kernels take d = 64 or 128. Another head dim (a multiple of 8 up to
-    128) is zero-padded to the next of those: padded columns add exact
-    zeros to every score and to D = rowsum(dO * O), and their gradients are
-    zero, so the first d columns are the gradients of the unpadded problem
-    (scale defaults to 1/sqrt of the unpadded d).
+    [B, H, Nk, d] (Nk may differ from Nq when not causal). Any strides with a
+    unit last dimension and 16-byte aligned rows are taken as they are
+    (attn_bwd_strided); d is a multiple of 8 up to 128. float32 inputs need
+    a float32 o and give float32 gradients. grad_dtype defaults to the input
+    dtype (torch.float32 is also accepted). The workspace (a uint8 tensor of
+    at least bwd_workspace_bytes(B, H, Nq, d) bytes) is taken from torch's
+    allocator when not given. Preallocated (dq, dk, dv) may be passed as
+    `grads`, with any strides of the same kind.
     """
     if q.dim() != 4 or k.dim() != 4 or o.shape != q.shape or dout.shape != q.shape or \
             v.shape != k.shape or (k.shape[0], k.shape[1], k.shape[3]) != \
             (q.shape[0], q.shape[1], q.shape[3]):
         raise ValueError("q, o, dout must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
-    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in (torch.float16,
-                                                                            torch.bfloat16):
-        raise ValueError("q, k, v, dout must share one dtype, float16 or bfloat16")
+    if not (q.dtype == k.dtype == v.dtype == dout.dtype) or q.dtype not in _TORCH_TO_ATTN:
+        raise ValueError("q, k, v, dout must share one dtype among float32/float16/bfloat16")
     tensors = (q, k, v, o, lse, dout)
     if not (q.is_cuda and all(x.device == q.device for x in tensors)):
         raise ValueError("all tensors must be on one GPU")
-    if not all(x.is_contiguous() for x in tensors):
-        raise ValueError("all tensors must be contiguous")
-    B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32:
-        raise ValueError("lse must be a [B, H, N] float32 tensor")
+    if any(x.stride(3) != 1 for x in (q, k, v, o, dout)):
+        raise ValueError("the last dimension must be contiguous")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if d % 8 or not 8 <= d <= 128:
+        raise ValueError("the head dim must be a multiple of 8 from 8 to 128")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous [B, H, Nq] float32 tensor")
     if o.dtype not in (q.dtype, torch.float32):
         raise ValueError("o must be in the input dtype or float32")
     if scale is None:
@@ -313,36 +330,24 @@ def attn_bwd(q, k, v, o, lse, dout, causal=False, scale=None, grad_dtype=None, w
     grad_dtype = grad_dtype or q.dtype
     if grad_dtype not in (q.dtype, torch.float32):
         raise ValueError("grad_dtype must be the input dtype or float32")
-    Nk = k.shape[2]
     if grads is None:
         grads = [torch.empty(x.shape, dtype=grad_dtype, device=q.device) for x in (q, k, v)]
     dq, dk, dv = grads
-    if any(g.shape != x.shape or g.dtype != grad_dtype or not g.is_contiguous() or
+    if any(g.shape != x.shape or g.dtype != grad_dtype or g.stride(3) != 1 or
            g.device != q.device for g, x in zip(grads, (q, k, v))):
-        raise ValueError("grads must be contiguous tensors shaped like q, k, v, of grad_dtype, "
-                         "on q's device")
-    if d not in (64, 128):
-        if d % 8 or not 8 <= d <= 128:
-            raise ValueError("the head dim must be a multiple of 8 from 8 to 128")
-        dp = 64 if d < 64 else 128
-
-        def pad(x):
-            return torch.nn.functional.pad(x, (0, dp - d))
-
-        padded = attn_bwd(pad(q), pad(k), pad(v), pad(o), lse, pad(dout), causal, scale,
-                          grad_dtype, workspace)
-        for g, x in zip(grads, padded):
-            g.copy_(x[..., :d])
-        return dq, dk, dv
-    need = bwd_workspace_bytes(B, H, N, d)
+        raise ValueError("grads must be tensors shaped like q, k, v, of grad_dtype, with a unit "
+                         "last stride, on q's device")
+    need = bwd_workspace_bytes(B, H, Nq, d)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = attn_bwd_qk_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N,
-                         Nk, d, causal, scale, _TORCH_TO_ATTN[q.dtype], _TORCH_TO_ATTN[o.dtype],
-                         _TORCH_TO_ATTN[grad_dtype], workspace.data_ptr(),
-                         workspace.numel() * workspace.element_size(), stream)
+    st = attn_bwd_strided_raw(
+        q.data_ptr(), q.stride()[:3], k.data_ptr(), k.stride()[:3], v.data_ptr(), v.stride()[:3],
+        o.data_ptr(), o.stride()[:3], lse.data_ptr(), dout.data_ptr(), dout.stride()[:3],
+        dq.data_ptr(), dq.stride()[:3], dk.data_ptr(), dk.stride()[:3], dv.data_ptr(),
+        dv.stride()[:3], B, H, Nq, Nk, d, causal, scale, _TORCH_TO_ATTN[q.dtype],
+        _TORCH_TO_ATTN[o.dtype], _TORCH_TO_ATTN[grad_dtype], workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), stream)
     if st != 0:
         msg = status_string(st)
         if st == 5:

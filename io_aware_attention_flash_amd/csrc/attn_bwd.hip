@@ -76,14 +76,23 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
-  const float *lse;
+  const float *lse;  // [B][H][Nq] contiguous
   void *dq, *dk, *dv;
-  f32x2 *ld;  // workspace: (L * log2 e, D) per query row
+  f32x2 *ld;  // workspace: (L * log2 e, D) per query row, [B][H][Nq]
+  // element strides of (batch, head, row) of each tensor; columns are unit-stride
+  int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
   int Nq, Nk;  // query rows and keys per head (equal when causal)
-  int BH;
+  int BH, H;
+  int d;       // head dimension; columns d .. D-1 of the kernels read as zeros
   float qk;     // scale * log2(e)
   float scale;  // applied to dQ and dK
 };
+
+// Element offset of head bh = b * H + h in a tensor with strides st.
+__device__ __forceinline__ int64_t head_off(const int64_t *st, int bh, int H) {
+  const int b = bh / H;
+  return (int64_t)b * st[0] + (int64_t)(bh - b * H) * st[1];
+}
 
 // ---------------------------------------------------------------------------
 // LDS tiles: rows of D 16-bit elements, 16-byte chunks XOR-swizzled by row so
@@ -226,28 +235,39 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-// Tile of R rows x D 16-bit elements, copied by all 256 threads: instruction
-// c fills 16-byte slots c*256 + tid; slot s holds physical chunk s % CPR of
-// row s / CPR, i.e. logical chunk (s % CPR) ^ swz(row). One instruction spans
-// a whole number of swizzle periods (16 rows), so the lane's source offset
-// is that of c = 0 plus c * 4096 bytes.
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a source offset past any range
+
+// Tile of R rows x D 16-bit elements of a matrix with row stride sn, copied by
+// all 256 threads: instruction c fills 16-byte slots c*256 + tid; slot s holds
+// physical chunk s % CPR of tile row s / CPR, i.e. logical chunk
+// (s % CPR) ^ swz(row). One instruction spans a whole number of swizzle
+// periods (16 rows), so the lane's source offset is that of c = 0 plus c rows
+// strides of RPI rows. A lane whose logical chunk starts at or past column d
+// reads from an offset beyond the range, which returns zeros: the columns
+// d .. D-1 of the tile are zero without any instruction in the loops.
 template <int D, int R>
 struct TileCopy {
   static constexpr int CPR = D / 8;
-  static constexpr int INS = R * CPR / kThreads;
-  static_assert(INS * kThreads == R * CPR && (kThreads / CPR) % 16 == 0, "tile copy shape");
-  __device__ static uint32_t src_offset(int tid) {
-    const int row = tid / CPR;
-    return row * D * 2 + (((tid % CPR) ^ swz<D>(row)) << 4);
+  static constexpr int RPI = kThreads / CPR;  // rows per instruction
+  static constexpr int INS = R / RPI;
+  static_assert(INS * RPI == R && RPI % 16 == 0, "tile copy shape");
+  uint32_t off0;  // source byte offset of instruction 0, or kOutOfRange
+  uint32_t step;  // bytes between instructions: RPI rows
+  __device__ void init(int tid, int64_t sn, int d) {
+    const int row = tid / CPR, lc = (tid % CPR) ^ swz<D>(row);
+    off0 = lc * 8 < d ? (uint32_t)(row * sn * 2 + lc * 16) : kOutOfRange;
+    step = (uint32_t)(RPI * sn * 2);
   }
-  // rows [r0, r0 + R) of a head of N rows into the tile at `lds`.
-  __device__ static void issue(const uint16_t *head, int r0, int N, uint16_t *lds, uint32_t voff,
-                               int wave) {
-    const int rows = min(N - r0, R);
-    const u32x4 rs = make_rsrc(head + (size_t)r0 * D, (uint32_t)(rows > 0 ? rows : 0) * D * 2);
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 64 * 16);
+  // rows [r0, min(r0 + R, n)) of the matrix at `base` into the tile at `lds`.
+  __device__ void issue(const uint16_t *base, int64_t sn, int r0, int n, int d, uint16_t *lds,
+                        int wave) const {
+    const int rows = min(n - r0, R);
+    const uint32_t bytes = rows > 0 ? (uint32_t)(((int64_t)(rows - 1) * sn + d) * 2) : 0u;
+    const u32x4 rs = make_rsrc(base + (rows > 0 ? (int64_t)r0 * sn : 0), bytes);
+    const uint32_t ldsb = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 64 * 16);
 #pragma unroll
-    for (int c = 0; c < INS; ++c) dma16(rs, base + c * kThreads * 16, voff + c * kThreads * 16);
+    for (int c = 0; c < INS; ++c)
+      dma16(rs, ldsb + c * kThreads * 16, off0 == kOutOfRange ? kOutOfRange : off0 + c * step);
   }
 };
 
@@ -261,51 +281,48 @@ __device__ __forceinline__ float f16_hi_to_f32(uint32_t w) {
 
 // ---------------------------------------------------------------------------
 // bwd_prep: LD[r] = (L_r * log2 e, D_r = sum_c dO[r,c] O[r,c]) for every
-// query row r (B*H*N rows). 16 lanes per row, 8 columns each (d = 128), or
-// 8 lanes per row (d = 64).
+// query row r = bh * Nq + i (B*H*Nq rows). LPR lanes per row, 8 columns each
+// (16 lanes for D = 128, 8 for D = 64); lanes whose columns start at or past d
+// add nothing. IN is the element type of dO (attn_dtype: fp32, fp16 or bf16);
+// O is that type or fp32.
 // ---------------------------------------------------------------------------
-template <int D, bool IS_BF16, bool O_F32>
+template <int IN>
+__device__ __forceinline__ void load8(const void *base, int64_t e, float (&x)[8]) {
+  if constexpr (IN == ATTN_F32) {
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + e);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(base) + e + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = a[i], x[4 + i] = b[i];
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (IN == ATTN_BF16) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+      } else {
+        x[2 * i] = f16_lo_to_f32(w[i]);
+        x[2 * i + 1] = f16_hi_to_f32(w[i]);
+      }
+    }
+  }
+}
+
+template <int D, int IN, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t r = gid / LPR;
   const int part = (int)(gid % LPR);
   float acc = 0.f;
-  if (r < rows) {
-    const size_t e0 = (size_t)r * D + part * 8;
-    const u32x4 dw = *reinterpret_cast<const u32x4 *>(
-        reinterpret_cast<const uint16_t *>(p.dout) + e0);
-    float dof[8];
+  if (r < rows && part * 8 < p.d) {
+    const int bh = (int)(r / p.Nq), i = (int)(r - (int64_t)bh * p.Nq);
+    float dof[8], of[8];
+    load8<IN>(p.dout, head_off(p.dos, bh, p.H) + (int64_t)i * p.dos[2] + part * 8, dof);
+    load8<O_F32 ? (int)ATTN_F32 : IN>(p.o, head_off(p.os, bh, p.H) + (int64_t)i * p.os[2] + part * 8,
+                                       of);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (IS_BF16) {
-        dof[2 * i] = __uint_as_float(dw[i] << 16);
-        dof[2 * i + 1] = __uint_as_float(dw[i] & 0xffff0000u);
-      } else {
-        dof[2 * i] = f16_lo_to_f32(dw[i]);
-        dof[2 * i + 1] = f16_hi_to_f32(dw[i]);
-      }
-    }
-    if constexpr (O_F32) {
-      const f32x4 o0 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.o) + e0);
-      const f32x4 o1 = *reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(p.o) + e0 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc += dof[i] * o0[i] + dof[4 + i] * o1[i];
-    } else {
-      const u32x4 ow = *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(p.o) + e0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float lo, hi;
-        if constexpr (IS_BF16) {
-          lo = __uint_as_float(ow[i] << 16);
-          hi = __uint_as_float(ow[i] & 0xffff0000u);
-        } else {
-          lo = f16_lo_to_f32(ow[i]);
-          hi = f16_hi_to_f32(ow[i]);
-        }
-        acc += dof[2 * i] * lo + dof[2 * i + 1] * hi;
-      }
-    }
+    for (int c = 0; c < 8; ++c) acc += dof[c] * of[c];
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
@@ -341,17 +358,19 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   const int bh = blockIdx.x - kbk * p.BH;
   const int Nq = p.Nq, Nk = p.Nk;
   const int k0 = kbk * kBlockK, kw0 = k0 + 32 * wave;
-  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + qhead;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + khead;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + khead;
-  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + qhead;
+  const int d = p.d;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head_off(p.qs, bh, p.H);
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head_off(p.ks, bh, p.H);
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head_off(p.vs, bh, p.H);
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head_off(p.dos, bh, p.H);
   const f32x2 *LDh = p.ld + (size_t)bh * Nq;
 
   uint16_t *vlds = lds;
   auto stage = [&](int s) { return lds + S::V_ELEMS + s * S::STAGE; };
 
-  const uint32_t qvoff = QCopy::src_offset(tid);
+  QCopy qc, dc;
+  qc.init(tid, p.qs[2], d);
+  dc.init(tid, p.dos[2], d);
   const int q_begin = CAUSAL ? k0 : 0;
   const int n_qt = (Nq - q_begin + kTileQ - 1) / kTileQ;
 
@@ -359,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   auto issue = [&](int it) {
     const int q0 = q_begin + it * kTileQ;
     uint16_t *st = stage(it & 1);
-    QCopy::issue(Qh, q0, Nq, st, qvoff, wave);
-    QCopy::issue(dOh, q0, Nq, st + S::TILE, qvoff, wave);
+    qc.issue(Qh, p.qs[2], q0, Nq, d, st, wave);
+    dc.issue(dOh, p.dos[2], q0, Nq, d, st + S::TILE, wave);
     if (wave == 0) {
       const int rows = min(Nq - q0, kTileQ);
       const u32x4 rs = make_rsrc(LDh + q0, (uint32_t)rows * 8);
@@ -369,17 +388,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   };
 
   // V block (this workgroup's 128 keys) into LDS, and the first query tile.
-  VCopy::issue(Vh, k0, Nk, vlds, VCopy::src_offset(tid), wave);
+  {
+    VCopy vc;
+    vc.init(tid, p.vs[2], d);
+    vc.issue(Vh, p.vs[2], k0, Nk, d, vlds, wave);
+  }
   issue(0);
 
   // K operand of S = Q K^T for this wave's keys: K[kw0 + l32][16kc + 8g ..].
   u32x4 kf[NKC];
   {
     const bool ok = kw0 + l32 < Nk;
-    const uint16_t *kr = Kh + (size_t)(ok ? kw0 + l32 : 0) * D + 8 * g;
+    const uint16_t *kr = Kh + (int64_t)(ok ? kw0 + l32 : 0) * p.ks[2] + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc)
-      kf[kc] = ok ? *reinterpret_cast<const u32x4 *>(kr + 16 * kc) : u32x4{0, 0, 0, 0};
+      kf[kc] = ok && 16 * kc + 8 * g < d ? *reinterpret_cast<const u32x4 *>(kr + 16 * kc)
+                                         : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) settle(kf[kc]);
   }
@@ -469,22 +493,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
 
   // dV^T / dK^T accumulators: lane holds key my_key, columns 32cb + 8j + 4g + 0..3.
   if (my_key < Nk) {
-    const size_t row = (size_t)bh * Nk + my_key;
+    const int64_t vrow = head_off(p.dvs, bh, p.H) + (int64_t)my_key * p.dvs[2];
+    const int64_t krow = head_off(p.dks, bh, p.H) + (int64_t)my_key * p.dks[2];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 32 * cb + 8 * j + 4 * g;
+        if (c >= d) continue;
         const f32x4 v4 = {dvt[cb][4 * j], dvt[cb][4 * j + 1], dvt[cb][4 * j + 2], dvt[cb][4 * j + 3]};
         const f32x4 k4 = {dkt[cb][4 * j] * p.scale, dkt[cb][4 * j + 1] * p.scale,
                           dkt[cb][4 * j + 2] * p.scale, dkt[cb][4 * j + 3] * p.scale};
         if constexpr (GRAD_F32) {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dv) + row * D + c) = v4;
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dk) + row * D + c) = k4;
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dv) + vrow + c) = v4;
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dk) + krow + c) = k4;
         } else {
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dv) + row * D + c) =
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dv) + vrow + c) =
               u32x2{pack2<IS_BF16>(v4[0], v4[1]), pack2<IS_BF16>(v4[2], v4[3])};
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dk) + row * D + c) =
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dk) + krow + c) =
               u32x2{pack2<IS_BF16>(k4[0], k4[1]), pack2<IS_BF16>(k4[2], k4[3])};
         }
       }
@@ -520,20 +546,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
   const int qb = CAUSAL ? nqb - 1 - t_ : t_;  // causal: longest first
   const int m0 = qb * kBlockQ, qw0 = m0 + 32 * wave;
   const int my_q = qw0 + l32;
-  const size_t qhead = (size_t)bh * Nq * D, khead = (size_t)bh * Nk * D;
-  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + qhead;
-  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + khead;
-  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + khead;
-  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + qhead;
+  const int d = p.d;
+  const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head_off(p.qs, bh, p.H);
+  const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head_off(p.ks, bh, p.H);
+  const uint16_t *Vh = reinterpret_cast<const uint16_t *>(p.v) + head_off(p.vs, bh, p.H);
+  const uint16_t *dOh = reinterpret_cast<const uint16_t *>(p.dout) + head_off(p.dos, bh, p.H);
 
-  const uint32_t kvoff = KCopy::src_offset(tid);
+  KCopy kc_, vc_;
+  kc_.init(tid, p.ks[2], d);
+  vc_.init(tid, p.vs[2], d);
   const int kend = CAUSAL ? min(Nk, m0 + kBlockQ) : Nk;
   const int n_kt = (kend + kTileK - 1) / kTileK;
   auto stage = [&](int s) { return lds + s * S::STAGE; };
   auto issue = [&](int it) {
     uint16_t *st = stage(it & 1);
-    KCopy::issue(Kh, it * kTileK, Nk, st, kvoff, wave);
-    KCopy::issue(Vh, it * kTileK, Nk, st + S::TILE, kvoff, wave);
+    kc_.issue(Kh, p.ks[2], it * kTileK, Nk, d, st, wave);
+    vc_.issue(Vh, p.vs[2], it * kTileK, Nk, d, st + S::TILE, wave);
   };
   issue(0);
 
@@ -541,11 +569,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
   u32x4 qf[NKC], df[NKC];
   {
     const bool ok = my_q < Nq;
-    const size_t r = (size_t)(ok ? my_q : 0) * D + 8 * g;
+    const int64_t rq = (int64_t)(ok ? my_q : 0) * p.qs[2] + 8 * g;
+    const int64_t rd = (int64_t)(ok ? my_q : 0) * p.dos[2] + 8 * g;
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      qf[kc] = ok ? *reinterpret_cast<const u32x4 *>(Qh + r + 16 * kc) : u32x4{0, 0, 0, 0};
-      df[kc] = ok ? *reinterpret_cast<const u32x4 *>(dOh + r + 16 * kc) : u32x4{0, 0, 0, 0};
+      const bool in = ok && 16 * kc + 8 * g < d;
+      qf[kc] = in ? *reinterpret_cast<const u32x4 *>(Qh + rq + 16 * kc) : u32x4{0, 0, 0, 0};
+      df[kc] = in ? *reinterpret_cast<const u32x4 *>(dOh + rd + 16 * kc) : u32x4{0, 0, 0, 0};
     }
   }
   f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
@@ -612,21 +642,220 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
 
   // dQ^T accumulators: lane holds query my_q, columns 32cb + 8j + 4g + 0..3.
   if (my_q < Nq) {
-    const size_t row = (size_t)bh * Nq + my_q;
+    const int64_t row = head_off(p.dqs, bh, p.H) + (int64_t)my_q * p.dqs[2];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = 32 * cb + 8 * j + 4 * g;
+        if (c >= d) continue;
         const f32x4 q4 = {dqt[cb][4 * j] * p.scale, dqt[cb][4 * j + 1] * p.scale,
                           dqt[cb][4 * j + 2] * p.scale, dqt[cb][4 * j + 3] * p.scale};
         if constexpr (GRAD_F32)
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dq) + row * D + c) = q4;
+          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dq) + row + c) = q4;
         else
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dq) + row * D + c) =
+          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dq) + row + c) =
               u32x2{pack2<IS_BF16>(q4[0], q4[1]), pack2<IS_BF16>(q4[2], q4[3])};
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs (the page's check of the backward in fp32): the same split on
+// v_mfma_f32_32x32x2_f32, everything in fp32. Tiles of 32 rows go through LDS
+// with plain strided loads (rows of D + 2 floats: the row-per-lane operand
+// reads hit 32 different banks); columns past d read as zeros.
+//
+// Contractions whose operand sits in a score tile held row-per-lane take
+// that tile straight from the registers: in a 32x32 accumulator, lane
+// (l32, g) holds element r of its column at row 8(r/4) + 4g + r%4, so step s
+// (of 16) of the contraction pairs k slot g with row 8(s/4) + 4g + s%4, and
+// the other operand is read from LDS at that row.
+// ---------------------------------------------------------------------------
+template <int D>
+struct F32Tile {
+  static constexpr int STR = D + 2;   // floats per LDS row
+  static constexpr int ELEMS = 32 * STR;
+};
+
+// Rows r0 .. r0+31 (those < n) of a strided fp32 matrix into an LDS tile;
+// other rows and columns >= d are zero.
+template <int D>
+__device__ __forceinline__ void load_tile_f32(float *t, const float *base, int64_t sn, int r0, int n,
+                                              int d, int tid) {
+  for (int e = tid; e < 32 * D / 4; e += kThreads) {
+    const int row = e / (D / 4), c = (e % (D / 4)) * 4;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (r0 + row < n && c < d) x = *reinterpret_cast<const f32x4 *>(base + (int64_t)(r0 + row) * sn + c);
+    float *dst = t + row * F32Tile<D>::STR + c;
+    dst[0] = x[0], dst[1] = x[1], dst[2] = x[2], dst[3] = x[3];
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_f32(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// dK, dV: one workgroup per (head, 128 keys), 4 waves x 32 keys; per 32-query
+// tile S = Q K^T and dP = dO V^T (lane: one key, 16 queries), P, dS, then
+// dV^T += dO^T P and dK^T += Q^T dS with P and dS from the registers.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_f32(BwdParams p) {
+  constexpr int NCB = D / 32, STR = F32Tile<D>::STR;
+  __shared__ float qt[F32Tile<D>::ELEMS], dot[F32Tile<D>::ELEMS];
+  __shared__ f32x2 ldt[32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int kbk = blockIdx.x / p.BH, bh = blockIdx.x - kbk * p.BH;
+  const int Nq = p.Nq, Nk = p.Nk, d = p.d;
+  const int k0 = kbk * kBlockK, kw0 = k0 + 32 * wave, my_key = kw0 + l32;
+  const float *Qh = static_cast<const float *>(p.q) + head_off(p.qs, bh, p.H);
+  const float *Kh = static_cast<const float *>(p.k) + head_off(p.ks, bh, p.H);
+  const float *Vh = static_cast<const float *>(p.v) + head_off(p.vs, bh, p.H);
+  const float *dOh = static_cast<const float *>(p.dout) + head_off(p.dos, bh, p.H);
+  const f32x2 *LDh = p.ld + (size_t)bh * Nq;
+  // K and V operands: row my_key, columns 2kk + g
+  float kf[D / 2], vf[D / 2];
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk) {
+    const int c = 2 * kk + g;
+    const bool ok = my_key < Nk && c < d;
+    kf[kk] = ok ? Kh[(int64_t)my_key * p.ks[2] + c] : 0.f;
+    vf[kk] = ok ? Vh[(int64_t)my_key * p.vs[2] + c] : 0.f;
+  }
+  f32x16 dvt[NCB], dkt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dvt[cb] = dkt[cb] = f32x16{};
+  const float qk = p.qk;
+  const int q_begin = CAUSAL ? k0 : 0;
+#pragma unroll 1
+  for (int q0 = q_begin; q0 < Nq; q0 += 32) {
+    __syncthreads();  // the previous tile is consumed
+    load_tile_f32<D>(qt, Qh, p.qs[2], q0, Nq, d, tid);
+    load_tile_f32<D>(dot, dOh, p.dos[2], q0, Nq, d, tid);
+    if (tid < 32) ldt[tid] = q0 + tid < Nq ? LDh[q0 + tid] : f32x2{0.f, 0.f};
+    __syncthreads();
+    if (CAUSAL && q0 + 31 < kw0) continue;  // every query before every key of this wave
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) {
+      sc = mfma_f32(qt[l32 * STR + 2 * kk + g], kf[kk], sc);
+      dp = mfma_f32(dot[l32 * STR + 2 * kk + g], vf[kk], dp);
+    }
+    // element r: query q0 + 8(r/4) + 4g + r%4, key my_key
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qi = 8 * (r >> 2) + 4 * g + (r & 3), qrow = q0 + qi;
+      const f32x2 ld = ldt[qi];
+      const bool keep = qrow < Nq && my_key < Nk && (!CAUSAL || my_key <= qrow);
+      const float pw = keep ? __builtin_amdgcn_exp2f(sc[r] * qk - ld[0]) : 0.f;
+      sc[r] = pw;                    // P
+      dp[r] = pw * (dp[r] - ld[1]);  // dS
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int qi = 8 * (st >> 2) + 4 * g + (st & 3);
+        dvt[cb] = mfma_f32(dot[qi * STR + 32 * cb + l32], sc[st], dvt[cb]);
+        dkt[cb] = mfma_f32(qt[qi * STR + 32 * cb + l32], dp[st], dkt[cb]);
+      }
+  }
+  // dV^T / dK^T: lane holds key my_key, columns 32cb + 8j + 4g + 0..3
+  if (my_key < Nk) {
+    float *dvr = static_cast<float *>(p.dv) + head_off(p.dvs, bh, p.H) + (int64_t)my_key * p.dvs[2];
+    float *dkr = static_cast<float *>(p.dk) + head_off(p.dks, bh, p.H) + (int64_t)my_key * p.dks[2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * cb + 8 * j + 4 * g;
+        if (c >= d) continue;
+        *reinterpret_cast<f32x4 *>(dvr + c) =
+            f32x4{dvt[cb][4 * j], dvt[cb][4 * j + 1], dvt[cb][4 * j + 2], dvt[cb][4 * j + 3]};
+        *reinterpret_cast<f32x4 *>(dkr + c) =
+            f32x4{dkt[cb][4 * j] * p.scale, dkt[cb][4 * j + 1] * p.scale,
+                  dkt[cb][4 * j + 2] * p.scale, dkt[cb][4 * j + 3] * p.scale};
+      }
+  }
+}
+
+// dQ: one workgroup per (head, 128 queries), 4 waves x 32 queries; per
+// 32-key tile S^T = K Q^T and dP^T = V dO^T (lane: one query, 16 keys), P,
+// dS, then dQ^T += K^T dS^T with dS from the registers.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_f32(BwdParams p) {
+  constexpr int NCB = D / 32, STR = F32Tile<D>::STR;
+  __shared__ float kt[F32Tile<D>::ELEMS], vt[F32Tile<D>::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int Nq = p.Nq, Nk = p.Nk, d = p.d;
+  const int nqb = (Nq + kBlockQ - 1) / kBlockQ;
+  const int t_ = blockIdx.x / p.BH, bh = blockIdx.x - t_ * p.BH;
+  const int qb = CAUSAL ? nqb - 1 - t_ : t_;  // causal: longest first
+  const int m0 = qb * kBlockQ, qw0 = m0 + 32 * wave, my_q = qw0 + l32;
+  const float *Qh = static_cast<const float *>(p.q) + head_off(p.qs, bh, p.H);
+  const float *Kh = static_cast<const float *>(p.k) + head_off(p.ks, bh, p.H);
+  const float *Vh = static_cast<const float *>(p.v) + head_off(p.vs, bh, p.H);
+  const float *dOh = static_cast<const float *>(p.dout) + head_off(p.dos, bh, p.H);
+  float qf[D / 2], df[D / 2];
+#pragma unroll
+  for (int kk = 0; kk < D / 2; ++kk) {
+    const int c = 2 * kk + g;
+    const bool ok = my_q < Nq && c < d;
+    qf[kk] = ok ? Qh[(int64_t)my_q * p.qs[2] + c] : 0.f;
+    df[kk] = ok ? dOh[(int64_t)my_q * p.dos[2] + c] : 0.f;
+  }
+  const f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
+  f32x16 dqt[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) dqt[cb] = f32x16{};
+  const float qk = p.qk;
+  const int kend = CAUSAL ? min(Nk, m0 + kBlockQ) : Nk;
+#pragma unroll 1
+  for (int key0 = 0; key0 < kend; key0 += 32) {
+    __syncthreads();
+    load_tile_f32<D>(kt, Kh, p.ks[2], key0, Nk, d, tid);
+    load_tile_f32<D>(vt, Vh, p.vs[2], key0, Nk, d, tid);
+    __syncthreads();
+    if (CAUSAL && key0 > qw0 + 31) continue;  // every key after every query of this wave
+    f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < D / 2; ++kk) {
+      sc = mfma_f32(kt[l32 * STR + 2 * kk + g], qf[kk], sc);
+      dp = mfma_f32(vt[l32 * STR + 2 * kk + g], df[kk], dp);
+    }
+    // element r: key key0 + 8(r/4) + 4g + r%4, query my_q
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool keep = key < Nk && my_q < Nq && (!CAUSAL || key <= my_q);
+      const float pw = keep ? __builtin_amdgcn_exp2f(sc[r] * qk - ldv[0]) : 0.f;
+      dp[r] = pw * (dp[r] - ldv[1]);  // dS
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int ki = 8 * (st >> 2) + 4 * g + (st & 3);
+        dqt[cb] = mfma_f32(kt[ki * STR + 32 * cb + l32], dp[st], dqt[cb]);
+      }
+  }
+  if (my_q < Nq) {
+    float *dqr = static_cast<float *>(p.dq) + head_off(p.dqs, bh, p.H) + (int64_t)my_q * p.dqs[2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = 32 * cb + 8 * j + 4 * g;
+        if (c >= d) continue;
+        *reinterpret_cast<f32x4 *>(dqr + c) =
+            f32x4{dqt[cb][4 * j] * p.scale, dqt[cb][4 * j + 1] * p.scale,
+                  dqt[cb][4 * j + 2] * p.scale, dqt[cb][4 * j + 3] * p.scale};
+      }
   }
 }
 
@@ -652,13 +881,64 @@ void pick2(bool causal, bool grad_f32, KernelFn &dkdv, KernelFn &dq) {
 }
 
 template <int D>
-PrepFn pick_prep(bool is_bf16, bool o_f32) {
-  if (is_bf16) return o_f32 ? bwd_prep<D, true, true> : bwd_prep<D, true, false>;
-  return o_f32 ? bwd_prep<D, false, true> : bwd_prep<D, false, false>;
+void pick_f32(bool causal, KernelFn &dkdv, KernelFn &dq) {
+  dkdv = causal ? bwd_dkdv_f32<D, true> : bwd_dkdv_f32<D, false>;
+  dq = causal ? bwd_dq_f32<D, true> : bwd_dq_f32<D, false>;
+}
+
+template <int D>
+PrepFn pick_prep(attn_dtype in, bool o_f32) {
+  if (in == ATTN_F32) return bwd_prep<D, ATTN_F32, true>;
+  if (in == ATTN_BF16) return o_f32 ? bwd_prep<D, ATTN_BF16, true> : bwd_prep<D, ATTN_BF16, false>;
+  return o_f32 ? bwd_prep<D, ATTN_F16, true> : bwd_prep<D, ATTN_F16, false>;
 }
 
 size_t ws_bytes(int64_t B, int64_t H, int64_t N) {
   return (((size_t)(B * H) * (size_t)N * 8) + 255) & ~(size_t)255;
+}
+
+int elem_bytes(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
+
+// Element strides of the (batch, head, row) dimensions of every tensor.
+struct BwdViews {
+  int64_t qs[3], ks[3], vs[3], os[3], dos[3], dqs[3], dks[3], dvs[3];
+};
+
+// The given strides, or those of a contiguous [B][H][n][d] tensor.
+void fill_strides(int64_t out[3], const int64_t *in, int64_t H, int64_t n, int64_t d) {
+  if (in) {
+    out[0] = in[0], out[1] = in[1], out[2] = in[2];
+  } else {
+    out[2] = d, out[1] = n * d, out[0] = H * n * d;
+  }
+}
+
+BwdViews contiguous_views(int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  BwdViews w;
+  fill_strides(w.qs, nullptr, H, Nq, d);
+  fill_strides(w.ks, nullptr, H, Nk, d);
+  fill_strides(w.vs, nullptr, H, Nk, d);
+  fill_strides(w.os, nullptr, H, Nq, d);
+  fill_strides(w.dos, nullptr, H, Nq, d);
+  fill_strides(w.dqs, nullptr, H, Nq, d);
+  fill_strides(w.dks, nullptr, H, Nk, d);
+  fill_strides(w.dvs, nullptr, H, Nk, d);
+  return w;
+}
+
+// A strided view is usable when every offset is non-negative and below 2^47
+// elements, rows do not overlap (row stride >= d), every row starts 16-byte
+// aligned, and a tile of 128 rows spans less than 2^31 bytes (the range of a
+// buffer descriptor).
+bool view_ok(const void *ptr, const int64_t s[3], int64_t B, int64_t H, int64_t n, int64_t d,
+             int eb) {
+  if (s[0] < 0 || s[1] < 0 || s[2] < d) return false;
+  const int64_t lim = int64_t(1) << 47;
+  if (s[0] > lim / B || s[1] > lim / H || s[2] > lim / n) return false;
+  if ((reinterpret_cast<uintptr_t>(ptr) & 15) != 0) return false;
+  for (int i = 0; i < 3; ++i)
+    if ((s[i] * eb) % 16 != 0) return false;
+  return s[2] * eb * 128 < (int64_t(1) << 31);
 }
 
 // Argument checks shared by the backward's entry points; no HIP call.
@@ -672,11 +952,30 @@ attn_status bwd_check(const void *q, const void *k, const void *v, const void *o
   if (Nq > (int64_t(1) << 24) || Nk > (int64_t(1) << 24) || B * H > (int64_t(1) << 24))
     return ATTN_ERR_SHAPE;
   if (causal && Nq != Nk) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
-  if (o_dtype != in_dtype && o_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
-  if (grad_dtype != in_dtype && grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if (d < 8 || d > 128 || d % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (in_dtype == ATTN_F32) {
+    if (o_dtype != ATTN_F32 || grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  } else {
+    if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
+    if (o_dtype != in_dtype && o_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+    if (grad_dtype != in_dtype && grad_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  }
   if (!(scale >= 0.f) || !isfinite(scale)) return ATTN_ERR_SCALE;
+  return ATTN_OK;
+}
+
+// Checks of the eight views (strided entry point).
+attn_status views_check(const void *q, const void *k, const void *v, const void *o,
+                        const void *dout, const void *dq, const void *dk, const void *dv,
+                        const BwdViews &w, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                        int64_t d, attn_dtype in_dtype, attn_dtype o_dtype,
+                        attn_dtype grad_dtype) {
+  const int ei = elem_bytes(in_dtype), eo = elem_bytes(o_dtype), eg = elem_bytes(grad_dtype);
+  if (!view_ok(q, w.qs, B, H, Nq, d, ei) || !view_ok(k, w.ks, B, H, Nk, d, ei) ||
+      !view_ok(v, w.vs, B, H, Nk, d, ei) || !view_ok(o, w.os, B, H, Nq, d, eo) ||
+      !view_ok(dout, w.dos, B, H, Nq, d, ei) || !view_ok(dq, w.dqs, B, H, Nq, d, eg) ||
+      !view_ok(dk, w.dks, B, H, Nk, d, eg) || !view_ok(dv, w.dvs, B, H, Nk, d, eg))
+    return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }
 
@@ -684,12 +983,13 @@ attn_status bwd_check(const void *q, const void *k, const void *v, const void *o
 // the launch sizes before any HIP call.
 attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
-                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
-                    float scale, attn_dtype in_dtype, attn_dtype o_dtype,
+                    const BwdViews &w, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                    int causal, float scale, attn_dtype in_dtype, attn_dtype o_dtype,
                     attn_dtype grad_dtype, void *ld, void *stream) {
+  const int64_t D = d <= 64 ? 64 : 128;  // the kernels' head dim; columns past d are zeros
   const int64_t nkb = (Nk + kBlockK - 1) / kBlockK, nqb = (Nq + kBlockQ - 1) / kBlockQ;
   const int64_t rows = B * H * Nq;
-  const int64_t lpr = d / 8;
+  const int64_t lpr = D / 8;
   const int64_t prep_blocks = (rows * lpr + 255) / 256;
   if (nkb * B * H > INT32_MAX || nqb * B * H > INT32_MAX || prep_blocks > INT32_MAX)
     return ATTN_ERR_SHAPE;
@@ -705,23 +1005,28 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
   p.dk = dk;
   p.dv = dv;
   p.ld = reinterpret_cast<f32x2 *>(ld);
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = w.qs[i], p.ks[i] = w.ks[i], p.vs[i] = w.vs[i], p.os[i] = w.os[i];
+    p.dos[i] = w.dos[i], p.dqs[i] = w.dqs[i], p.dks[i] = w.dks[i], p.dvs[i] = w.dvs[i];
+  }
   p.Nq = (int)Nq;
   p.Nk = (int)Nk;
   p.BH = (int)(B * H);
+  p.H = (int)H;
+  p.d = (int)d;
   p.qk = (float)((double)scale * 1.4426950408889634);
   p.scale = scale;
 
-  const bool bf16 = in_dtype == ATTN_BF16, grad_f32 = grad_dtype == ATTN_F32;
-  const bool o_f32 = o_dtype == ATTN_F32;
+  const bool grad_f32 = grad_dtype == ATTN_F32, o_f32 = o_dtype == ATTN_F32;
   KernelFn fdkdv, fdq;
-  PrepFn fprep;
-  if (d == 64) {
-    fprep = pick_prep<64>(bf16, o_f32);
-    if (bf16) pick2<64, true>(causal != 0, grad_f32, fdkdv, fdq);
+  const PrepFn fprep = D == 64 ? pick_prep<64>(in_dtype, o_f32) : pick_prep<128>(in_dtype, o_f32);
+  if (in_dtype == ATTN_F32) {
+    if (D == 64) pick_f32<64>(causal != 0, fdkdv, fdq); else pick_f32<128>(causal != 0, fdkdv, fdq);
+  } else if (D == 64) {
+    if (in_dtype == ATTN_BF16) pick2<64, true>(causal != 0, grad_f32, fdkdv, fdq);
     else pick2<64, false>(causal != 0, grad_f32, fdkdv, fdq);
   } else {
-    fprep = pick_prep<128>(bf16, o_f32);
-    if (bf16) pick2<128, true>(causal != 0, grad_f32, fdkdv, fdq);
+    if (in_dtype == ATTN_BF16) pick2<128, true>(causal != 0, grad_f32, fdkdv, fdq);
     else pick2<128, false>(causal != 0, grad_f32, fdkdv, fdq);
   }
   hipStream_t st = (hipStream_t)stream;
@@ -784,7 +1089,7 @@ extern "C" {
 
 size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B < 1 || H < 1 || N < 1 || N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return 0;
-  if (d != 64 && d != 128) return 0;
+  if (d < 8 || d > 128 || d % 8 != 0) return 0;
   return ws_bytes(B, H, N);
 }
 
@@ -801,7 +1106,37 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
   const size_t need = ws_bytes(B, H, Nq);
   if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
     return ATTN_ERR_WORKSPACE;
-  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, in_dtype,
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, contiguous_views(H, Nq, Nk, d), B, H, Nq, Nk,
+                 d, causal, scale, in_dtype, o_dtype, grad_dtype, workspace, stream);
+}
+
+attn_status attn_bwd_strided(const void *q, const int64_t *q_strides, const void *k,
+                             const int64_t *k_strides, const void *v, const int64_t *v_strides,
+                             const void *o, const int64_t *o_strides, const float *lse,
+                             const void *dout, const int64_t *dout_strides, void *dq,
+                             const int64_t *dq_strides, void *dk, const int64_t *dk_strides,
+                             void *dv, const int64_t *dv_strides, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                             attn_dtype in_dtype, attn_dtype o_dtype, attn_dtype grad_dtype,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+  attn_status st = bwd_check(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale,
+                             in_dtype, o_dtype, grad_dtype);
+  if (st != ATTN_OK) return st;
+  BwdViews w;
+  fill_strides(w.qs, q_strides, H, Nq, d);
+  fill_strides(w.ks, k_strides, H, Nk, d);
+  fill_strides(w.vs, v_strides, H, Nk, d);
+  fill_strides(w.os, o_strides, H, Nq, d);
+  fill_strides(w.dos, dout_strides, H, Nq, d);
+  fill_strides(w.dqs, dq_strides, H, Nq, d);
+  fill_strides(w.dks, dk_strides, H, Nk, d);
+  fill_strides(w.dvs, dv_strides, H, Nk, d);
+  st = views_check(q, k, v, o, dout, dq, dk, dv, w, B, H, Nq, Nk, d, in_dtype, o_dtype, grad_dtype);
+  if (st != ATTN_OK) return st;
+  const size_t need = ws_bytes(B, H, Nq);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15) != 0)
+    return ATTN_ERR_WORKSPACE;
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, w, B, H, Nq, Nk, d, causal, scale, in_dtype,
                  o_dtype, grad_dtype, workspace, stream);
 }
 
@@ -817,8 +1152,8 @@ attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const 
   void *ld = nullptr;
   st = scratch_address(&ld);
   if (st != ATTN_OK) return st;
-  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, in_dtype,
-                 o_dtype, grad_dtype, ld, stream);
+  return bwd_run(q, k, v, o, lse, dout, dq, dk, dv, contiguous_views(H, Nq, Nk, d), B, H, Nq, Nk,
+                 d, causal, scale, in_dtype, o_dtype, grad_dtype, ld, stream);
 }
 
 attn_status attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,

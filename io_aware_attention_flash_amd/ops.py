@@ -25,11 +25,20 @@ from . import binding
 _NS = "io_aware_attention_flash"
 
 
+def _usable(x):
+    """x itself when the kernels can read it in place (unit last stride, rows
+    16-byte aligned), else a contiguous copy."""
+    e = x.element_size()
+    if x.stride(-1) == 1 and x.data_ptr() % 16 == 0 and all((st * e) % 16 == 0
+                                                            for st in x.stride()[:-1]):
+        return x
+    return x.contiguous()
+
+
 @torch.library.custom_op(_NS + "::fwd", mutates_args=())
 def _fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
          scale: float) -> tuple[torch.Tensor, torch.Tensor]:
-    o, lse = binding.attn_fwd(q.contiguous(), k.contiguous(), v.contiguous(), causal=causal,
-                              scale=scale)
+    o, lse = binding.attn_fwd(_usable(q), _usable(k), _usable(v), causal=causal, scale=scale)
     return o, lse
 
 
@@ -44,8 +53,8 @@ def _fwd_fake(q, k, v, causal, scale):
 def _bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
          dout: torch.Tensor, causal: bool,
          scale: float) -> tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    return tuple(binding.attn_bwd(q.contiguous(), k.contiguous(), v.contiguous(), o.contiguous(),
-                                  lse.contiguous(), dout.contiguous(), causal=causal, scale=scale))
+    return tuple(binding.attn_bwd(_usable(q), _usable(k), _usable(v), _usable(o), lse.contiguous(),
+                                  _usable(dout), causal=causal, scale=scale))
 
 
 @_bwd.register_fake
@@ -72,8 +81,8 @@ _fwd.register_autograd(_backward, setup_context=_setup_context)
 
 
 def flash_attn_func(q, k, v, causal=False, scale=None):
-    """softmax(scale q k^T [+ causal mask]) v for [B, H, N, d] bf16/fp16
-    tensors on the GPU, differentiable in q, k and v. scale defaults to
+    """softmax(scale q k^T [+ causal mask]) v for [B, H, N, d] bf16, fp16 or
+    fp32 tensors on the GPU, differentiable in q, k and v. scale defaults to
     1/sqrt(d)."""
     if scale is None:
         scale = 1.0 / q.shape[-1] ** 0.5

@@ -141,7 +141,8 @@ def test_workspace_entry_validates_first(lib, args, code):
     (2, 32, 4096, 128, 2 * 32 * 4096 * 8),
     (1, 1, 1, 64, 256),                 # rounded up to 256 bytes
     (1, 3, 77, 64, 256 * ((3 * 77 * 8 + 255) // 256)),
-    (1, 1, 128, 96, 0), (0, 1, 128, 64, 0), (1, 1, (1 << 24) + 1, 64, 0),
+    (1, 1, 128, 96, 1024),              # any multiple of 8 up to 128
+    (1, 1, 128, 100, 0), (1, 1, 128, 136, 0), (0, 1, 128, 64, 0), (1, 1, (1 << 24) + 1, 64, 0),
 ])
 def test_bwd_workspace_bytes(lib, B, H, N, d, want):
     assert binding.bwd_workspace_bytes(B, H, N, d) == want
@@ -153,9 +154,10 @@ def test_bwd_workspace_bytes(lib, B, H, N, d, want):
     (dict(dk=0), 1), (dict(dv=0), 1),
     # shapes
     (dict(B=0), 2), (dict(N=0), 2), (dict(N=(1 << 24) + 1), 2),
-    # head dims and dtypes: fp32 inputs, O or gradient types outside {in, F32}
-    (dict(d=96), 3), (dict(i=0, o_t=0, g_t=0), 3), (dict(i=2, o_t=1), 3),
-    (dict(i=1, g_t=2), 3), (dict(i=5), 3),
+    # head dims and dtypes: d not a multiple of 8 in [8, 128]; fp32 inputs with
+    # a 16-bit O or gradients; O or gradient types outside {in, F32}
+    (dict(d=100), 3), (dict(d=136), 3), (dict(d=0), 3), (dict(i=0, o_t=2, g_t=0), 3),
+    (dict(i=0, o_t=0, g_t=1), 3), (dict(i=2, o_t=1), 3), (dict(i=1, g_t=2), 3), (dict(i=5), 3),
     # scale
     (dict(scale=float("nan")), 4), (dict(scale=-1.0), 4),
     # workspace: missing, too small, misaligned
@@ -215,7 +217,7 @@ def test_row_softmax_error_paths_need_no_gpu(lib, args, code):
 
 @pytest.mark.parametrize("args,code", [
     (dict(Nk=0), 2), (dict(Nq=0), 2), (dict(causal=1), 2),   # causal needs Nq == Nk
-    (dict(d=96), 3), (dict(ws=0), 6),
+    (dict(d=100), 3), (dict(ws=0), 6),
 ])
 def test_bwd_qk_error_paths_need_no_gpu(lib, args, code):
     a = dict(B=1, H=1, Nq=64, Nk=80, d=64, causal=0, ws=P)
@@ -228,7 +230,7 @@ def test_bwd_qk_error_paths_need_no_gpu(lib, args, code):
 @pytest.mark.parametrize("args,code", [
     (dict(q=0), 1), (dict(dv=0), 1),
     (dict(Nq=0), 2), (dict(causal=1), 2),                    # causal needs Nq == Nk
-    (dict(d=96), 3), (dict(i=0, o_t=0, g_t=0), 3),
+    (dict(d=100), 3), (dict(i=0, o_t=2, g_t=0), 3),
     (dict(scale=-1.0), 4),
     # B*H*Nq rows of 8 bytes beyond the 16 MiB static scratch (2^21 rows)
     (dict(B=2, H=16, Nq=(1 << 16) + 1, Nk=128), 7), (dict(B=1, H=1, Nq=(1 << 21) + 1, Nk=64), 7),
@@ -243,3 +245,31 @@ def test_bwd_noalloc_error_paths_need_no_gpu(lib, args, code):
                                       a["i"], a["o_t"], a["g_t"])
     assert st == code, (args, st)
     assert "static scratch" in binding.status_string(7)
+
+
+@pytest.mark.parametrize("args,code", [
+    (dict(q=0), 1), (dict(dk=0), 1),
+    (dict(Nq=0), 2), (dict(causal=1), 2),
+    (dict(d=12), 3), (dict(i=0, o_t=2), 3),
+    (dict(q=P + 8), 3),                                   # misaligned base
+    (dict(q_st=(-4096, 4096, 64)), 3),                    # negative stride
+    (dict(k_st=(1 << 20, 1 << 14, 32)), 3),               # row stride < d
+    (dict(v_st=(1 << 20, 1 << 14, 68)), 3),               # row not 16-byte aligned (bf16)
+    (dict(dq_st=(1 << 20, 1 << 14, 66)), 3),              # gradient row not aligned (fp32)
+    (dict(o_st=(1 << 47, 1 << 14, 64)), 3),               # offsets beyond 2^47 elements
+    (dict(do_st=(1 << 30, 1 << 24, 1 << 23)), 3),         # 128 rows span >= 2^31 bytes
+    (dict(scale=float("nan")), 4),
+    (dict(ws=0), 6),
+])
+def test_bwd_strided_error_paths_need_no_gpu(lib, args, code):
+    """attn_bwd_strided rejects every bad argument before any HIP call (each
+    case here is invalid, so nothing is launched)."""
+    a = dict(q=P, dk=P, q_st=None, k_st=None, v_st=None, o_st=None, do_st=None, dq_st=None,
+             B=2, H=2, Nq=64, Nk=80, d=64, causal=0, scale=0.125, i=2, o_t=0, g_t=0, ws=P)
+    a.update(args)
+    st = binding.attn_bwd_strided_raw(a["q"] or None, a["q_st"], P, a["k_st"], P, a["v_st"], P,
+                                      a["o_st"], P, P, a["do_st"], P, a["dq_st"], a["dk"] or None,
+                                      None, P, None, a["B"], a["H"], a["Nq"], a["Nk"], a["d"],
+                                      a["causal"], a["scale"], a["i"], a["o_t"], a["g_t"],
+                                      a["ws"] or None, 1 << 20)
+    assert st == code, (args, st)

@@ -37,8 +37,12 @@ from io_aware_attention_flash_amd.inputs import WORKLOADS, make_dout, make_qkv
 
 pytestmark = pytest.mark.gpu
 
-U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
-DT = {"f16": torch.float16, "bf16": torch.bfloat16}
+U = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11,
+     # fp32 inputs round nothing to a narrower type; the unit covers fp32
+     # accumulation over up to a few thousand terms and exp2 of scores whose
+     # own fp32 error is amplified by their size (|s * scale| up to ~10)
+     "f32": 2.0 ** -16}
+DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
 
 def setup_module(module):
@@ -275,7 +279,8 @@ def test_bwd_cross_attention(case):
 
 # ------------------------------------------- head dims reached by padding
 ODD_D = [
-    # (B, H, Nq, Nk, d, dtype, causal): the binding zero-pads d to 64 or 128
+    # (B, H, Nq, Nk, d, dtype, causal): the kernels run at 64 or 128 columns
+    # and read the columns past d as zeros
     (1, 2, 200, 200, 96, "bf16", True),
     (2, 1, 130, 130, 80, "f16", False),
     (1, 2, 97, 97, 40, "bf16", True),
@@ -301,6 +306,83 @@ def test_bwd_padded_head_dim(case):
     ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
     terms, extra = _terms(q, k, v, dout, causal, scale)
     check_grads(got, ref, terms, extra, U[dt], "padded d %s" % (case,))
+
+
+# ------------------------------------------------------------- fp32 inputs
+F32_CASES = [
+    # (B, H, Nq, Nk, d, causal): the page's test shape, a larger head dim,
+    # padded head dims, cross-attention
+    (2, 4, 256, 256, 64, False), (2, 4, 256, 256, 64, True), (1, 2, 300, 300, 128, True),
+    (1, 1, 97, 97, 40, True), (1, 2, 130, 130, 96, False), (1, 2, 64, 200, 128, False),
+    (1, 1, 1, 1, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", F32_CASES, ids=lambda c: "B%dH%dNq%dNk%dd%d_%s" % (
+    c[:5] + ("causal" if c[5] else "full",)))
+def test_bwd_f32(case):
+    """fp32 inputs run in fp32 throughout: within the rounding bound above
+    (u = 2^-16) and within the page's ~1e-3 for fp32 ("4.4 Writing GPU
+    Kernels with Triton", section "Kernel 5: FlashAttention Backward", its
+    test notes); O and LSE from the oracle (fp32)."""
+    B, H, Nq, Nk, d, causal = case
+    _say("case", case)
+    q = make_qkv(B, H, Nq, d, "f32", 1.0, seed=19)[0]
+    _, k, v = make_qkv(B, H, Nk, d, "f32", 1.0, seed=20)
+    dout = make_dout(B, H, Nq, d, "f32", seed=19)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, causal, scale)
+    got = gpu_bwd(q, k, v, o, lse, dout, causal, scale)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    terms, extra = _terms(q, k, v, dout, causal, scale)
+    check_grads(got, ref, terms, extra, U["f32"], "f32 %s" % (case,))
+    for g, r in zip(got, ref):
+        assert float(np.abs(g.double().numpy() - r).max()) <= 1e-3
+
+
+def test_bwd_f32_end_to_end():
+    """fp32 forward then fp32 backward."""
+    B, H, N, d = 1, 2, 257, 128
+    q, k, v, dout = _inputs(B, H, N, d, "f32", 1.0, seed=21)
+    scale = _scale(d)
+    dev = torch.device("cuda:0")
+    o, lse = binding.attn_fwd(q.to(dev), k.to(dev), v.to(dev), causal=True, scale=scale)
+    got = gpu_bwd(q, k, v, o, lse, dout, True, scale)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=True, scale=scale)
+    for g, r in zip(got, ref):
+        assert float(np.abs(g.double().numpy() - r).max()) <= 1e-3
+
+
+# ----------------------------------------------------------- strided views
+@pytest.mark.parametrize("dt,d,causal", [("bf16", 128, True), ("f16", 64, False),
+                                         ("bf16", 80, False), ("f32", 128, True)])
+def test_bwd_strided_views(dt, d, causal):
+    """q, k, v, dout, o and the gradients as [B, N, H, d] tensors seen as
+    [B, H, N, d] (the layout of a fused projection): the same kernels with
+    other addresses, so the gradients equal the contiguous call's bit for
+    bit, and meet the oracle."""
+    B, H, N = 2, 3, 203
+    q, k, v, dout = _inputs(B, H, N, d, dt, 1.0, seed=22)
+    scale = _scale(d)
+    o, lse = _oracle_o_lse(q, k, v, causal, scale)
+    dev = torch.device("cuda:0")
+
+    def bnhd(x):
+        return x.to(dev).transpose(1, 2).contiguous().transpose(1, 2)
+
+    want = binding.attn_bwd(*(x.to(dev) for x in (q, k, v, o, lse, dout)), causal=causal,
+                            scale=scale, grad_dtype=torch.float32)
+    gbuf = [torch.full((B, N, H, d), float("nan"), device=dev) for _ in range(3)]
+    grads = [g.transpose(1, 2) for g in gbuf]
+    got = binding.attn_bwd(bnhd(q), bnhd(k), bnhd(v), bnhd(o), lse.to(dev), bnhd(dout),
+                           causal=causal, scale=scale, grad_dtype=torch.float32, grads=grads)
+    torch.cuda.synchronize()
+    for a, b in zip(got, want):
+        assert not a.is_contiguous()
+        assert torch.equal(a, b)
+    ref = oracle.attn_bwd_oracle(q, k, v, dout, causal=causal, scale=scale)
+    terms, extra = _terms(q, k, v, dout, causal, scale)
+    check_grads([g.cpu() for g in got], ref, terms, extra, U[dt], "strided %s d=%d" % (dt, d))
 
 
 def test_bwd_head_dim_out_of_range():
