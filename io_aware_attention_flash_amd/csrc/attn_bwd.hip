@@ -73,6 +73,17 @@ static_assert(kTileK == 32 || kTileK == 64 || kTileK == 128, "dQ key tile");
 constexpr int kBwdLookahead = ATTN_CFG_BWD_LOOKAHEAD;
 static_assert(kBwdLookahead >= 1 && kBwdLookahead <= 3, "lookahead range");
 constexpr float kLog2e = 1.4426950408889634f;
+// Gradient stores with the non-temporal hint or plain. Each lane stores its own
+// 8- or 16-byte pieces of a row, not whole cache lines, and streaming them past
+// the caches measured 9% slower at the causal N=4096 d=128 workload: plain.
+#ifndef ATTN_CFG_BWD_NONTEMPORAL
+#define ATTN_CFG_BWD_NONTEMPORAL 0
+#endif
+
+template <class T>
+__device__ __forceinline__ void store_grad(T *dst, const T &val) {
+  if (ATTN_CFG_BWD_NONTEMPORAL) __builtin_nontemporal_store(val, dst); else *dst = val;
+}
 
 struct BwdParams {
   const void *q, *k, *v, *o, *dout;
@@ -505,13 +516,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
         const f32x4 k4 = {dkt[cb][4 * j] * p.scale, dkt[cb][4 * j + 1] * p.scale,
                           dkt[cb][4 * j + 2] * p.scale, dkt[cb][4 * j + 3] * p.scale};
         if constexpr (GRAD_F32) {
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dv) + vrow + c) = v4;
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dk) + krow + c) = k4;
+          store_grad(reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dv) + vrow + c), v4);
+          store_grad(reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dk) + krow + c), k4);
         } else {
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dv) + vrow + c) =
-              u32x2{pack2<IS_BF16>(v4[0], v4[1]), pack2<IS_BF16>(v4[2], v4[3])};
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dk) + krow + c) =
-              u32x2{pack2<IS_BF16>(k4[0], k4[1]), pack2<IS_BF16>(k4[2], k4[3])};
+          store_grad(reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dv) + vrow + c),
+                     u32x2{pack2<IS_BF16>(v4[0], v4[1]), pack2<IS_BF16>(v4[2], v4[3])});
+          store_grad(reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dk) + krow + c),
+                     u32x2{pack2<IS_BF16>(k4[0], k4[1]), pack2<IS_BF16>(k4[2], k4[3])});
         }
       }
     }
@@ -652,10 +663,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
         const f32x4 q4 = {dqt[cb][4 * j] * p.scale, dqt[cb][4 * j + 1] * p.scale,
                           dqt[cb][4 * j + 2] * p.scale, dqt[cb][4 * j + 3] * p.scale};
         if constexpr (GRAD_F32)
-          *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dq) + row + c) = q4;
+          store_grad(reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.dq) + row + c), q4);
         else
-          *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dq) + row + c) =
-              u32x2{pack2<IS_BF16>(q4[0], q4[1]), pack2<IS_BF16>(q4[2], q4[3])};
+          store_grad(reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.dq) + row + c),
+                     u32x2{pack2<IS_BF16>(q4[0], q4[1]), pack2<IS_BF16>(q4[2], q4[3])});
       }
     }
   }

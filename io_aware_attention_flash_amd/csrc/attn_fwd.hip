@@ -231,6 +231,18 @@ using Tile16 = Shape16<D, D == 128 ? ATTN_CFG_FWD_WAVES_D128 : ATTN_CFG_FWD_WAVE
 #ifndef ATTN_CFG_CAUSAL_SHORT_FIRST
 #define ATTN_CFG_CAUSAL_SHORT_FIRST 0
 #endif
+// Causal workgroups take a pair of query tiles (long + short, 1) or one
+// tile each, longest first (0).
+#ifndef ATTN_CFG_CAUSAL_PAIRS
+#define ATTN_CFG_CAUSAL_PAIRS 1
+#endif
+// Stores of O with the non-temporal hint (streamed past L2 and the Infinity
+// Cache, which then keep more of the K/V tiles the workgroups re-read) or
+// plain. The epilogue writes whole 128-byte lines; the hint measured +2.5% to
+// +3.8% at the causal N=4096 d=128 workload.
+#ifndef ATTN_CFG_O_NONTEMPORAL
+#define ATTN_CFG_O_NONTEMPORAL 1
+#endif
 
 // Rows of the online softmax are rescaled only when their maximum grows by
 // more than this many powers of two; otherwise exponentials are taken
@@ -1035,7 +1047,10 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
       const u32x4 val =
           *reinterpret_cast<const u32x4 *>(stage + row * OS::ROWB + ((c ^ OS::swz(row)) << 4));
       if (r0 + row < N)
-        *reinterpret_cast<u32x4 *>(obase + (size_t)row * D * OS::E + ps * OS::ROWB + c * 16) = val;
+      {
+        u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (size_t)row * D * OS::E + ps * OS::ROWB + c * 16);
+        if (ATTN_CFG_O_NONTEMPORAL) __builtin_nontemporal_store(val, dst); else *dst = val;
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -1057,7 +1072,7 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
   const int w = blockIdx.x;
   int t, bh;
   if ((p.BH & 7) == 0) {
-    const int per_head = CAUSAL ? (p.nq + 1) >> 1 : p.nq;
+    const int per_head = CAUSAL && ATTN_CFG_CAUSAL_PAIRS ? (p.nq + 1) >> 1 : p.nq;
     const int j = w >> 3;
     const int hl = j / per_head;
     t = j - hl * per_head;
@@ -1065,6 +1080,10 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
   } else {
     t = w / p.BH;
     bh = w - t * p.BH;
+  }
+  if (CAUSAL && !ATTN_CFG_CAUSAL_PAIRS) {
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, p.nq - 1 - t, false, -1);
+    return;
   }
   if (!CAUSAL) {
     attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
@@ -1375,7 +1394,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   const unsigned threads = f32_path ? kThreads : l16.threads;
   const int64_t nq = (N + block_m - 1) / block_m;
   // Causal bf16/fp16 workgroups take two query tiles each (long + short).
-  const int64_t grid = (causal && !f32_path ? (nq + 1) / 2 : nq) * B * H;
+  const int64_t grid = (causal && !f32_path && ATTN_CFG_CAUSAL_PAIRS ? (nq + 1) / 2 : nq) * B * H;
   if (grid > INT32_MAX) return ATTN_ERR_SHAPE;
 
   FwdParams p;

@@ -56,6 +56,23 @@ KNOBS = {
                                               "b1h16_n16384_d128_bf16_sigma3_causal"],
                                    what="causal workgroups run their short query tile first "
                                         "(1) or their long one (0)"),
+    "fwd_causal_pairs": dict(macro="ATTN_CFG_CAUSAL_PAIRS", values=[1, 0], pass_="fwd",
+                             workloads=["b2h32_n4096_d128_bf16_causal",
+                                        "b1h16_n16384_d128_bf16_sigma3_causal"],
+                             what="causal workgroups take pairs of query tiles (1) or one tile "
+                                  "each, longest first (0)"),
+    "fwd_o_nontemporal": dict(macro="ATTN_CFG_O_NONTEMPORAL", values=[1, 0], pass_="fwd",
+                              workloads=["b2h32_n4096_d128_bf16_causal",
+                                         "b8h12_n3000_d64_f16"],
+                              what="stores of O with the non-temporal hint (1) or plain (0)"),
+    "bwd_nontemporal": dict(macro="ATTN_CFG_BWD_NONTEMPORAL", values=[0, 1], pass_="bwd",
+                            workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                            what="the backward's gradient stores with the non-temporal hint (1) "
+                                 "or plain (0)"),
+    "gen_o_nontemporal": dict(macro="ATTN_CFG_GEN_O_NONTEMPORAL", values=[0, 1], pass_="general",
+                              workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                              what="the general kernel's stores of O with the non-temporal hint "
+                                   "(1) or plain (0)"),
     "fwd_lookahead": dict(macro="ATTN_CFG_LOOKAHEAD", values=[3, 2, 4], pass_="fwd",
                           workloads=["b2h32_n4096_d128_bf16_causal",
                                      "b1h16_n16384_d128_bf16_sigma3_causal"],
