@@ -231,6 +231,11 @@ using Tile16 = Shape16<D, D == 128 ? ATTN_CFG_FWD_WAVES_D128 : ATTN_CFG_FWD_WAVE
 #ifndef ATTN_CFG_CAUSAL_SHORT_FIRST
 #define ATTN_CFG_CAUSAL_SHORT_FIRST 0
 #endif
+// Copies of the query tile with the non-temporal hint (1; each query row is
+// read once) or plain (0).
+#ifndef ATTN_CFG_Q_NONTEMPORAL
+#define ATTN_CFG_Q_NONTEMPORAL 0
+#endif
 // Causal workgroups take a pair of query tiles (long + short, 1) or one
 // tile each, longest first (0).
 #ifndef ATTN_CFG_CAUSAL_PAIRS
@@ -307,6 +312,13 @@ __device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_ti
 // it is refilled). M0 carries the LDS address; nothing else here uses it.
 __device__ __forceinline__ void dma16_to_lds(u32x4 rsrc, uint32_t lds_byte, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_byte), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+// The same with the non-temporal hint, for data read once (the query tile).
+__device__ __forceinline__ void dma16_to_lds_nt(u32x4 rsrc, uint32_t lds_byte, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
                :
                : "s"(lds_byte), "v"(voff), "s"(rsrc)
                : "memory", "m0");
@@ -533,8 +545,13 @@ struct Pipe16 {
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
                      (uint32_t)__builtin_amdgcn_readfirstlane(rows * D * 2), (uint32_t)kBufferFlags};
 #pragma unroll
-    for (int c = 0; c < S::Q_INS; ++c)
-      dma16_to_lds(r, lds_wave + S::RING_ELEMS * 2 + c * S::INS_BYTES, k_dma[0] + c * S::INS_BYTES);
+    for (int c = 0; c < S::Q_INS; ++c) {
+      const uint32_t dst = lds_wave + S::RING_ELEMS * 2 + c * S::INS_BYTES;
+      if (ATTN_CFG_Q_NONTEMPORAL)
+        dma16_to_lds_nt(r, dst, k_dma[0] + c * S::INS_BYTES);
+      else
+        dma16_to_lds(r, dst, k_dma[0] + c * S::INS_BYTES);
+    }
   }
   __device__ __forceinline__ void issue_k(int t) const {
     const u32x4 r = k_rsrc(t);

@@ -65,6 +65,12 @@ KNOBS = {
                               workloads=["b2h32_n4096_d128_bf16_causal",
                                          "b8h12_n3000_d64_f16"],
                               what="stores of O with the non-temporal hint (1) or plain (0)"),
+    "fwd_q_nontemporal": dict(macro="ATTN_CFG_Q_NONTEMPORAL", values=[0, 1], pass_="fwd",
+                              workloads=["b2h32_n4096_d128_bf16_causal",
+                                         "b1h16_n16384_d128_bf16_sigma3_causal",
+                                         "b8h12_n3000_d64_f16"],
+                              what="copies of the query tile with the non-temporal hint (1) or "
+                                   "plain (0)"),
     "bwd_nontemporal": dict(macro="ATTN_CFG_BWD_NONTEMPORAL", values=[0, 1], pass_="bwd",
                             workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
                             what="the backward's gradient stores with the non-temporal hint (1) "
