@@ -428,13 +428,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
 #pragma unroll 1
   for (int it = 0; it < n_qt; ++it) {
     const int q0 = q_begin + it * kTileQ;
-    if (it + 1 < n_qt) {
-      issue(it + 1);
-      if (wave == 0) wait_vmcnt<2 * QCopy::INS + 1>(); else wait_vmcnt<2 * QCopy::INS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // Tile it has landed (this wave's copies, then everyone's after the
+    // barrier), and every wave is done with tile it - 1, whose stage the
+    // copies of tile it + 1 then refill while tile it is computed: one
+    // barrier per tile.
+    wait_vmcnt<0>();
     lds_barrier();
+    if (it + 1 < n_qt) issue(it + 1);
     const uint16_t *qt = stage(it & 1), *dot = qt + S::TILE;
     const f32x4 *ldt = reinterpret_cast<const f32x4 *>(qt + 2 * S::TILE);  // (L2, D) pairs
     // Whole tile above this wave's keys (causal): nothing to add.
@@ -499,7 +499,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
             }
           });
     }
-    lds_barrier();  // stage it & 1 is refilled by the next iteration's copies
   }
 
   // dV^T / dK^T accumulators: lane holds key my_key, columns 32cb + 8j + 4g + 0..3.
@@ -605,13 +604,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
 
 #pragma unroll 1
   for (int it = 0; it < n_kt; ++it) {
-    if (it + 1 < n_kt) {
-      issue(it + 1);
-      wait_vmcnt<2 * KCopy::INS>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // As in bwd_dkdv: wait for tile it, one barrier, then refill the stage of
+    // tile it - 1 with tile it + 1 while tile it is computed.
+    wait_vmcnt<0>();
     lds_barrier();
+    if (it + 1 < n_kt) issue(it + 1);
     const uint16_t *kt = stage(it & 1), *vt = kt + S::TILE;
 #pragma unroll
     for (int kb = 0; kb < kTileK / 32; ++kb) {
@@ -648,7 +645,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
             [&](int i, const u32x4 &a) { dqt[i % NCB] = mfma<IS_BF16>(a, sf[i / NCB], dqt[i % NCB]); });
       }
     }
-    lds_barrier();
   }
 
   // dQ^T accumulators: lane holds query my_q, columns 32cb + 8j + 4g + 0..3.
