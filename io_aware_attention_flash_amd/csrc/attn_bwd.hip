@@ -11,8 +11,10 @@
 // query-parallel kernel owns dQ, and neither writes the other's rows, so
 // there are no atomics and the result is deterministic.
 //
-// Three launches on the caller's stream:
-//   bwd_prep : LD[row] = (L * log2(e), D) per query row, into the workspace.
+// Two launches on the caller's stream for bf16/fp16 inputs (dQ first, then
+// dK/dV), three for fp32 (bwd_prep, dK/dV, dQ):
+//   bwd_prep : LD[row] = (L * log2(e), D) per query row, into the workspace;
+//              for 16-bit inputs bwd_dq does this step for its own rows.
 //   bwd_dkdv : one workgroup per (head, 128 keys); 4 waves of 32 keys each
 //              loop over 32-query tiles. Per tile and wave, on the matrix
 //              cores (v_mfma_f32_32x32x16, fp32 accumulate):
@@ -23,7 +25,8 @@
 //   bwd_dq   : one workgroup per (head, 128 queries); 4 waves of 32 queries
 //              loop over 64-key tiles: S^T = K Q^T, P, dP^T = V dO^T,
 //              dS, dQ^T += K^T dS^T. Q and dO stay in registers; K and V
-//              tiles stream through a two-stage LDS ring.
+//              tiles stream through a two-stage LDS ring. Its rows' D comes
+//              from dO (already in registers) and O, read once.
 // P and dS enter the matrix cores in the input type (bf16 or fp16), as the
 // page casts them to the operand type; S, P, dP, dS and every accumulator
 // are fp32. In both loops every MFMA's LDS operands are read a fixed number
@@ -95,6 +98,7 @@ struct BwdParams {
   int Nq, Nk;  // query rows and keys per head (equal when causal)
   int BH, H;
   int d;       // head dimension; columns d .. D-1 of the kernels read as zeros
+  int o_f32;   // O is fp32 (else the input type)
   float qk;     // scale * log2(e)
   float scale;  // applied to dQ and dK
 };
@@ -315,6 +319,21 @@ __device__ __forceinline__ void load8(const void *base, int64_t e, float (&x)[8]
         x[2 * i] = f16_lo_to_f32(w[i]);
         x[2 * i + 1] = f16_hi_to_f32(w[i]);
       }
+    }
+  }
+}
+
+// Eight packed 16-bit values (bf16 or fp16) as fp32 (exact).
+template <bool IS_BF16>
+__device__ __forceinline__ void unpack8(const u32x4 &w, float (&x)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (IS_BF16) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      x[2 * i] = f16_lo_to_f32(w[i]);
+      x[2 * i + 1] = f16_hi_to_f32(w[i]);
     }
   }
 }
@@ -588,14 +607,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
       df[kc] = in ? *reinterpret_cast<const u32x4 *>(dOh + rd + 16 * kc) : u32x4{0, 0, 0, 0};
     }
   }
-  f32x2 ldv = my_q < Nq ? p.ld[(size_t)bh * Nq + my_q] : f32x2{0.f, 0.f};
+  // This kernel runs first and does the preprocessing step for its rows:
+  // D = sum_c dO_c O_c over the columns this lane holds in df (16kc + 8g ..
+  // +7), the other half-wave's columns added by one swap, and L * log2 e.
+  // Both go to LD for the dK/dV kernel that runs next.
+  float dd = 0.f, l2 = 0.f;
+  if (my_q < Nq) {
+    const int64_t ro = head_off(p.os, bh, p.H) + (int64_t)my_q * p.os[2] + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      if (16 * kc + 8 * g >= d) continue;
+      float of[8], dof[8];
+      if (p.o_f32) load8<ATTN_F32>(p.o, ro + 16 * kc, of);
+      else load8<IS_BF16 ? (int)ATTN_BF16 : (int)ATTN_F16>(p.o, ro + 16 * kc, of);
+      unpack8<IS_BF16>(df[kc], dof);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) dd += dof[c] * of[c];
+    }
+    l2 = p.lse[(size_t)bh * Nq + my_q] * kLog2e;
+  }
+  dd += __shfl_xor(dd, 32);
+  if (g == 0 && my_q < Nq) p.ld[(size_t)bh * Nq + my_q] = f32x2{l2, dd};
 #pragma unroll
   for (int kc = 0; kc < NKC; ++kc) {
     settle(qf[kc]);
     settle(df[kc]);
   }
-  settle(ldv);
-  const float l2 = ldv[0], dd = ldv[1];
   const TrAddr<D> ta = tr_addr<D>(lane);
   f32x16 dqt[NCB];
 #pragma unroll
@@ -893,12 +930,6 @@ void pick_f32(bool causal, KernelFn &dkdv, KernelFn &dq) {
   dq = causal ? bwd_dq_f32<D, true> : bwd_dq_f32<D, false>;
 }
 
-template <int D>
-PrepFn pick_prep(attn_dtype in, bool o_f32) {
-  if (in == ATTN_F32) return bwd_prep<D, ATTN_F32, true>;
-  if (in == ATTN_BF16) return o_f32 ? bwd_prep<D, ATTN_BF16, true> : bwd_prep<D, ATTN_BF16, false>;
-  return o_f32 ? bwd_prep<D, ATTN_F16, true> : bwd_prep<D, ATTN_F16, false>;
-}
 
 size_t ws_bytes(int64_t B, int64_t H, int64_t N) {
   return (((size_t)(B * H) * (size_t)N * 8) + 255) & ~(size_t)255;
@@ -986,8 +1017,8 @@ attn_status views_check(const void *q, const void *k, const void *v, const void 
   return ATTN_OK;
 }
 
-// The three launches, with LD rows (8 bytes per query row) at `ld`. Checks
-// the launch sizes before any HIP call.
+// The launches, with LD rows (8 bytes per query row) at `ld`. Checks the
+// launch sizes before any HIP call.
 attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
                     const float *lse, const void *dout, void *dq, void *dk, void *dv,
                     const BwdViews &w, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
@@ -1021,12 +1052,12 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
   p.BH = (int)(B * H);
   p.H = (int)H;
   p.d = (int)d;
+  p.o_f32 = o_dtype == ATTN_F32;
   p.qk = (float)((double)scale * 1.4426950408889634);
   p.scale = scale;
 
-  const bool grad_f32 = grad_dtype == ATTN_F32, o_f32 = o_dtype == ATTN_F32;
+  const bool grad_f32 = grad_dtype == ATTN_F32;
   KernelFn fdkdv, fdq;
-  const PrepFn fprep = D == 64 ? pick_prep<64>(in_dtype, o_f32) : pick_prep<128>(in_dtype, o_f32);
   if (in_dtype == ATTN_F32) {
     if (D == 64) pick_f32<64>(causal != 0, fdkdv, fdq); else pick_f32<128>(causal != 0, fdkdv, fdq);
   } else if (D == 64) {
@@ -1037,17 +1068,29 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
     else pick2<128, false>(causal != 0, grad_f32, fdkdv, fdq);
   }
   hipStream_t st = (hipStream_t)stream;
-  int64_t rows_arg = rows;
-  void *pargs[] = {&p, &rows_arg};
-  hipError_t err = hipLaunchKernel(reinterpret_cast<const void *>(fprep), dim3((unsigned)prep_blocks),
-                                   dim3(256), pargs, 0, st);
   void *args[] = {&p};
-  if (err == hipSuccess)
-    err = hipLaunchKernel(reinterpret_cast<const void *>(fdkdv), dim3((unsigned)(nkb * B * H)),
-                          dim3(kThreads), args, 0, st);
-  if (err == hipSuccess)
+  hipError_t err = hipSuccess;
+  if (in_dtype == ATTN_F32) {
+    // prep, then dK/dV and dQ
+    int64_t rows_arg = rows;
+    void *pargs[] = {&p, &rows_arg};
+    const PrepFn fprep = D == 64 ? bwd_prep<64, ATTN_F32, true> : bwd_prep<128, ATTN_F32, true>;
+    err = hipLaunchKernel(reinterpret_cast<const void *>(fprep), dim3((unsigned)prep_blocks),
+                          dim3(256), pargs, 0, st);
+    if (err == hipSuccess)
+      err = hipLaunchKernel(reinterpret_cast<const void *>(fdkdv), dim3((unsigned)(nkb * B * H)),
+                            dim3(kThreads), args, 0, st);
+    if (err == hipSuccess)
+      err = hipLaunchKernel(reinterpret_cast<const void *>(fdq), dim3((unsigned)(nqb * B * H)),
+                            dim3(kThreads), args, 0, st);
+  } else {
+    // dQ (which writes LD for its rows), then dK/dV
     err = hipLaunchKernel(reinterpret_cast<const void *>(fdq), dim3((unsigned)(nqb * B * H)),
                           dim3(kThreads), args, 0, st);
+    if (err == hipSuccess)
+      err = hipLaunchKernel(reinterpret_cast<const void *>(fdkdv), dim3((unsigned)(nkb * B * H)),
+                            dim3(kThreads), args, 0, st);
+  }
   if (err != hipSuccess) {
     attn_internal::set_last_hip_error((int)err);
     return ATTN_ERR_HIP;

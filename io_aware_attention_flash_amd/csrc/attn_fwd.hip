@@ -1293,17 +1293,22 @@ Launch16 launch16(attn_dtype in, bool out_f32, bool causal, bool conv_v) {
 // The tile of a problem. The pages key their autotuning on the sequence
 // length, the head dimension and the mask; here two compiled tiles per head
 // dimension compete: 8 waves (one 256-row workgroup per CU; d=128: 64-key
-// tiles, d=64: 128-key) and 4 waves (two 128-row workgroups per CU; d=128:
-// 32-key tiles, d=64: 64-key). Measured at full occupancy, the 8-wave tile
+// tiles, d=64: 128-key) and 4 waves (128-row workgroups; d=128: 32-key
+// tiles, two per CU; d=64: 64-key tiles, whose 48 KB of LDS and at most 168
+// VGPRs let three share a CU). Measured at full occupancy, the 8-wave tile
 // is faster per unit of work (5% at d=64, 10% at d=128), but the grid runs
 // in whole rounds of workgroups: a last round that is only partly filled
 // leaves CUs idle for a whole workgroup's time, and with 4-wave tiles a
 // last round of at most one workgroup per CU runs each alone on its CU,
 // faster (taken as 0.6 of a round). Each tile's cost is its number of
-// rounds so weighted, times its per-unit cost; the cheaper one is taken
-// (io_aware_attention_flash_amd/sweep.py measured every tile on workloads
-// with whole and partial last rounds; this rule picks the faster tile on
-// each of them).
+// rounds so weighted, times its per-unit cost; the cheaper one is taken.
+// The rounds are counted at two 4-wave workgroups per CU for both head
+// dimensions: the constants were fitted to measurements
+// (io_aware_attention_flash_amd/sweep.py timed every tile on workloads with
+// whole and partial last rounds; this rule picks the fastest tile, or one
+// within 0.3% of it, on each), and counting three at d=64 with the same
+// constants would pick the 4-wave tile at B4 H16 N2048, where it is 2%
+// slower.
 constexpr int kCUs = 256;
 
 double tile_cost(int64_t units, int wg_per_cu, double unit_cost) {
