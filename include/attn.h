@@ -159,10 +159,12 @@ size_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d);
  *   dQ_i  = scale sum_j dS_ij K_j,  dK_j = scale sum_i dS_ij Q_i,
  *   dV_j  = sum_i P_ij dO_i.
  *
- * P is rebuilt tile by tile from LSE; no N x N tensor is written. A first
- * pass writes (LSE * log2 e, D) per row into the workspace; a key-parallel
- * kernel then writes dK and dV, and a query-parallel kernel writes dQ (no
- * atomics: the result is deterministic).
+ * P is rebuilt tile by tile from LSE; no N x N tensor is written. The
+ * preprocessing step writes (LSE * log2 e, D) per row into the workspace: for
+ * bf16/fp16 inputs the query-parallel kernel that writes dQ does it for its
+ * rows and runs first, for fp32 inputs a separate first pass does it; a
+ * key-parallel kernel then writes dK and dV from those rows (no atomics: the
+ * result is deterministic).
  *
  * q, k, v, dout : device, [B][H][N][d] contiguous, element type in_dtype
  *                 (BF16, F16 or F32).
