@@ -28,9 +28,9 @@
 //    A operand of QK^T, V through transposing reads (ds_read_b64_tr_b16)
 //    as the A operand of O^T. bf16 V is converted to fp16 in place in LDS.
 //  * each iteration is one stream of MFMAs (QK^T of the next tile, then P.V
-//    of this one) with the softmax work spread across it: on gfx950 one wave
-//    cannot keep the MFMA pipe busy by itself, and two waves that each mix
-//    MFMAs with their own vector work hide that work best.
+//    of this one) with the softmax work spread across it: with operands read
+//    from LDS and vector work between the MFMAs, two waves per SIMD that
+//    each mix MFMAs with their own vector work keep the pipe busiest.
 //  * fp32 inputs use a separate kernel on v_mfma_f32_32x32x2_f32.
 #include <hip/hip_runtime.h>
 
@@ -62,12 +62,23 @@ struct FwdParams {
   const void *v;     // V as the kernel reads it (the fp16 copy when a first pass made one)
   const void *v_in;  // V as the caller passed it
   void *o;
-  float *lse;
+  float *lse;        // [B][H][N] contiguous
+  // Element strides of (batch, head, row) of each tensor (columns are
+  // unit-stride); vs for v, vis for v_in. The fp32 kernel takes contiguous
+  // tensors only.
+  int64_t qs[3], ks[3], vs[3], vis[3], os[3];
   int N;         // sequence length
   int nq;        // query tiles per (batch, head)
   int BH;        // batch * heads
+  int H;         // heads
   float qk;      // scale * log2(e), >= FLT_MIN
 };
+
+// Element offset of head bh = b * H + h in a tensor with strides st.
+__device__ __forceinline__ int64_t head_off(const int64_t *st, int bh, int H) {
+  const int b = bh / H;
+  return (int64_t)b * st[0] + (int64_t)(bh - b * H) * st[1];
+}
 
 // Work item of this workgroup: (bh, query tile). Workgroups are dispatched
 // in id order and handed to the 8 XCDs round-robin, so id w runs on XCD
@@ -288,19 +299,23 @@ __device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
 constexpr int kBufferFlags = 0x00020000;
 
 // Buffer descriptor (four SGPR words) of tile t (keys t*BN ..) of one
-// head's K or V, cut to the keys that exist (empty for tiles past the last
-// one visited), so reads beyond the cut return zeros and touch no memory.
-// Every input is wave-uniform; readfirstlane says so to the compiler, which
-// keeps the words in scalar registers.
+// head's K or V with rows rs elements apart, cut to the keys that exist
+// (empty for tiles past the last one visited), so reads beyond the cut
+// return zeros and touch no memory. Every input is wave-uniform;
+// readfirstlane says so to the compiler, which keeps the words in scalar
+// registers.
 template <class S>
-__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N) {
+__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N, int rs) {
   constexpr int BN = S::BN, D = S::D;
   const int keys = t < n_tiles ? min(N - t * BN, BN) : 0;
-  const uint16_t *base = keys > 0 ? head + (size_t)t * BN * D : head;
+  const uint16_t *base = keys > 0 ? head + (size_t)t * BN * (size_t)rs : head;
+  // the last key's row ends D elements after its start: (keys - 1) rows of
+  // rs elements and one of D (keys * D * 2 bytes for contiguous rows)
+  const uint32_t bytes = (uint32_t)(keys * rs * 2 - (keys > 0 ? (rs - D) * 2 : 0));
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,  // stride 0
-               (uint32_t)__builtin_amdgcn_readfirstlane(keys * D * 2), (uint32_t)kBufferFlags};
+               (uint32_t)__builtin_amdgcn_readfirstlane(bytes), (uint32_t)kBufferFlags};
 }
 
 // One buffer_load_dwordx4 ... lds: 16 bytes per lane from the descriptor at
@@ -326,16 +341,17 @@ __device__ __forceinline__ void dma16_to_lds_nt(u32x4 rsrc, uint32_t lds_byte, u
 
 // DMA of one K or V tile into an LDS stage. Instruction c fills the 16-byte
 // slots c*THREADS + tid: slot s holds physical chunk s % CPR of tile row
-// s / CPR, i.e. logical chunk (s % CPR) ^ swz(row). Instruction c covers the
-// c-th INS_BYTES of the tile, a whole number of swizzle periods, so its lane
-// offset is that of c = 0 plus c * INS_BYTES. The offset stays in a VGPR
-// (the descriptor's range check applies to it, not to an SGPR offset).
+// s / CPR, i.e. logical chunk (s % CPR) ^ swz(row). Instruction c covers
+// THREADS / CPR rows of the tile, a whole number of swizzle periods, so its
+// lane offset is that of c = 0 plus c * (THREADS / CPR) rows of rs elements.
+// The offset stays in a VGPR (the descriptor's range check applies to it,
+// not to an SGPR offset).
 template <int D, bool IS_V>
-__device__ __forceinline__ uint32_t dma_offset(int tid) {
+__device__ __forceinline__ uint32_t dma_offset(int tid, int rs) {
   constexpr int CPR = D / 8;
   const int row0 = tid / CPR;
   const int swz = IS_V ? swz_v<D>(row0) : swz_k<D>(row0);
-  return row0 * D * 2 + (((tid % CPR) ^ swz) << 4);
+  return (uint32_t)(row0 * rs * 2) + (((tid % CPR) ^ swz) << 4);
 }
 // Wait until at most N vector-memory instructions of this wave are
 // outstanding (they retire in order).
@@ -510,8 +526,10 @@ struct Pipe16 {
   int N, n_tiles, qrow, g, tid;
   uint32_t lds_wave;  // LDS byte address of the buffer plus 1024 * wave (uniform)
   // Source offsets of this thread's 16 bytes in copy instruction c (kept in
-  // registers: the descriptor's range check applies to them).
-  uint32_t k_dma[S::DMA_INS], v_dma[S::DMA_INS];
+  // registers: the descriptor's range check applies to them), and that of
+  // the query tile's first copy instruction.
+  uint32_t k_dma[S::DMA_INS], v_dma[S::DMA_INS], q_dma0;
+  int qrs, krs, vrs;  // row strides (elements) of Q, K and V
   float qk;
 
   __device__ __forceinline__ uint16_t *kstage(int par) const {
@@ -526,8 +544,8 @@ struct Pipe16 {
   // V_{j+1}, then K_{j+2}, into the stages V_{j-1} and K_j left (free since
   // the barrier that ended iteration j-1); a late step waits for V_{j+1}
   // and converts it (bf16); the iteration ends by waiting for K_{j+2}.
-  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<S>(Kh, t, n_tiles, N); }
-  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<S>(Vh, t, n_tiles, N); }
+  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<S>(Kh, t, n_tiles, N, krs); }
+  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<S>(Vh, t, n_tiles, N, vrs); }
   // Instruction c of the copy of K_t / V_t (descriptor r).
   __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
     constexpr int TB = S::TILE_BYTES;
@@ -540,17 +558,20 @@ struct Pipe16 {
   // Copy of the workgroup's query tile (rows m0 ..; rows past N read as 0).
   __device__ __forceinline__ void issue_q(const uint16_t *Qh, int m0) const {
     const int rows = min(N - m0, S::BLOCK_M);
-    const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * D);
+    const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * (size_t)qrs);
     const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
-                     (uint32_t)__builtin_amdgcn_readfirstlane(rows * D * 2), (uint32_t)kBufferFlags};
+                     (uint32_t)__builtin_amdgcn_readfirstlane(((rows - 1) * qrs + D) * 2),
+                     (uint32_t)kBufferFlags};
+    constexpr int RPI = S::THREADS / S::CPR;  // rows per copy instruction
 #pragma unroll
     for (int c = 0; c < S::Q_INS; ++c) {
       const uint32_t dst = lds_wave + S::RING_ELEMS * 2 + c * S::INS_BYTES;
+      const uint32_t off = q_dma0 + (uint32_t)(c * RPI * qrs * 2);
       if (ATTN_CFG_Q_NONTEMPORAL)
-        dma16_to_lds_nt(r, dst, k_dma[0] + c * S::INS_BYTES);
+        dma16_to_lds_nt(r, dst, off);
       else
-        dma16_to_lds(r, dst, k_dma[0] + c * S::INS_BYTES);
+        dma16_to_lds(r, dst, off);
     }
   }
   __device__ __forceinline__ void issue_k(int t) const {
@@ -806,15 +827,18 @@ __device__ __forceinline__ void run_wave(const Pipe16<S> &pp, RowState16<S::D> &
 // not depend on V); the returned sum of the bf16-rounded weights normalises
 // the new output. Inputs holding inf or NaN give non-finite outputs either
 // way.
-template <int D, bool CAUSAL>
-__device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, size_t head, int r0, int qrow,
+template <int D, bool CAUSAL, bool STRIDED>
+__device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, int bh, int r0, int qrow,
                                                 int g, int l32, const u32x4 *qf,
                                                 RowState16<D> &st) {
   constexpr int NKC = D / 16, NCB = D / 32;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const int N = p.N;
-  const uint16_t *Kh = static_cast<const uint16_t *>(p.k) + head;
-  const uint16_t *Vh = static_cast<const uint16_t *>(p.v_in) + head;
+  const size_t chead = (size_t)bh * (size_t)N * D;  // contiguous [B][H][N][D]
+  const uint16_t *Kh = static_cast<const uint16_t *>(p.k) + (STRIDED ? head_off(p.ks, bh, p.H) : (int64_t)chead);
+  const uint16_t *Vh =
+      static_cast<const uint16_t *>(p.v_in) + (STRIDED ? head_off(p.vis, bh, p.H) : (int64_t)chead);
+  const int64_t krs = STRIDED ? p.ks[2] : D, vrs = STRIDED ? p.vis[2] : D;
   const int kend = CAUSAL ? min(N, r0 + 32) : N;
   const float qk = p.qk, neg_m = st.neg_m;
   float l = 0.f;
@@ -824,7 +848,7 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, size_t head,
   for (int k0 = 0; k0 < kend; k0 += 32) {
     // S^T for keys k0 .. k0 + 31 (K operand row k0 + l32, as k_frag lays it out)
     const int key = k0 + l32;
-    const uint16_t *krow = Kh + (size_t)(key < N ? key : 0) * D + 8 * g;
+    const uint16_t *krow = Kh + (int64_t)(key < N ? key : 0) * krs + 8 * g;
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
@@ -859,7 +883,7 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, size_t head,
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int kk = k0 + 16 * t + 8 * (x >> 2) + 4 * g + (x & 3);
-          vv[x] = kk < N ? Vh[(size_t)kk * D + 32 * cb + l32] : 0u;
+          vv[x] = kk < N ? Vh[(int64_t)kk * vrs + 32 * cb + l32] : 0u;
         }
         const u32x4 a = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
                          vv[6] | (vv[7] << 16)};
@@ -905,7 +929,7 @@ struct OutStage {
 // prefetched: the previous tile of this workgroup (same head) already copied
 // this tile's Q, V_0, K_0 and K_1. next_qt >= 0: copy that tile's ones once
 // this tile's loop is done.
-template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
+template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V, bool STRIDED>
 __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int bh, int qt,
                                           bool prefetched, int next_qt) {
   constexpr int D = S::D;
@@ -923,24 +947,31 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 
   const int N = p.N;
   const int m0 = qt * S::BLOCK_M;
-  const size_t head = (size_t)bh * (size_t)N * D;
-  const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + head;
+  // Element offsets of this head and row strides: the tensors' own
+  // (STRIDED), or those of contiguous [B][H][N][D] tensors, as constants.
+  const size_t chead = (size_t)bh * (size_t)N * D;
+  const uint16_t *Qh = static_cast<const uint16_t *>(p.q) + (STRIDED ? head_off(p.qs, bh, p.H) : (int64_t)chead);
 
   Pipe16<S> pp;
   pp.lds = lds;
-  pp.Kh = static_cast<const uint16_t *>(p.k) + head;
-  pp.Vh = static_cast<const uint16_t *>(p.v) + head;
+  pp.Kh = static_cast<const uint16_t *>(p.k) + (STRIDED ? head_off(p.ks, bh, p.H) : (int64_t)chead);
+  pp.Vh = static_cast<const uint16_t *>(p.v) + (STRIDED ? head_off(p.vs, bh, p.H) : (int64_t)chead);
+  pp.qrs = STRIDED ? (int)p.qs[2] : D;
+  pp.krs = STRIDED ? (int)p.ks[2] : D;
+  pp.vrs = STRIDED ? (int)p.vs[2] : D;
   pp.la = lane_addr<D>(lane);
   pp.N = N;
   pp.g = g;
   pp.tid = tid;
   pp.qk = p.qk;
   pp.lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 1024);
+  constexpr int RPI = S::THREADS / S::CPR;  // tile rows per copy instruction
 #pragma unroll
   for (int c = 0; c < S::DMA_INS; ++c) {
-    pp.k_dma[c] = dma_offset<D, false>(tid) + c * S::INS_BYTES;
-    pp.v_dma[c] = dma_offset<D, true>(tid) + c * S::INS_BYTES;
+    pp.k_dma[c] = dma_offset<D, false>(tid, pp.krs) + (uint32_t)(c * RPI * pp.krs * 2);
+    pp.v_dma[c] = dma_offset<D, true>(tid, pp.vrs) + (uint32_t)(c * RPI * pp.vrs * 2);
   }
+  pp.q_dma0 = dma_offset<D, false>(tid, pp.qrs);
   // This lane's query row. Rows past N read zeros (the query tile's copy
   // descriptor is cut at N) and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
@@ -1017,7 +1048,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   if (pp.qrow < N && g == 0)
     p.lse[(size_t)bh * N + pp.qrow] = (st.m + log2_fast(l_safe)) * 0.69314718055994531f;
   if (IS_BF16 && __any(acc_not_finite<D>(st))) {
-    const float lb = sum_halves(redo_rows_bf16<D, CAUSAL>(p, head, r0, pp.qrow, g, l32, qf, st));
+    const float lb = sum_halves(redo_rows_bf16<D, CAUSAL, STRIDED>(p, bh, r0, pp.qrow, g, l32, qf, st));
     inv = 1.0f / (lb > 0.f ? lb : 1.f);
   }
   // O leaves through LDS. A lane holds one row, so stores straight from the
@@ -1031,7 +1062,9 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
                 "staging fits");
   uint8_t *stage = reinterpret_cast<uint8_t *>(lds + (S::OWN_STAGE ? S::RING_ELEMS + S::BLOCK_M * D : 0)) +
                    wave * OS::WAVE_BYTES;
-  uint8_t *obase = static_cast<uint8_t *>(p.o) + (head + (size_t)r0 * D) * OS::E;
+  const int64_t ors = STRIDED ? p.os[2] : D;
+  uint8_t *obase = static_cast<uint8_t *>(p.o) +
+                   ((STRIDED ? head_off(p.os, bh, p.H) : (int64_t)chead) + (int64_t)r0 * ors) * OS::E;
 #pragma unroll
   for (int ps = 0; ps < OS::PASSES; ++ps) {
     // This lane's row l32: 4-column pieces at 32cb + 8r4 + 4g.
@@ -1065,7 +1098,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
           *reinterpret_cast<const u32x4 *>(stage + row * OS::ROWB + ((c ^ OS::swz(row)) << 4));
       if (r0 + row < N)
       {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (size_t)row * D * OS::E + ps * OS::ROWB + c * 16);
+        u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (int64_t)row * ors * OS::E + ps * OS::ROWB + c * 16);
         if (ATTN_CFG_O_NONTEMPORAL) __builtin_nontemporal_store(val, dst); else *dst = val;
       }
     }
@@ -1083,7 +1116,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
 // start together, so each head's K/V stream through that XCD's L2 about once
 // rather than once per wave of workgroups. Otherwise ids run item-major,
 // head-minor.
-template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V>
+template <class S, bool IS_BF16, bool CAUSAL, bool OUT_F32, bool CONV_V, bool STRIDED>
 __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
   const int w = blockIdx.x;
@@ -1099,11 +1132,11 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
     bh = w - t * p.BH;
   }
   if (CAUSAL && !ATTN_CFG_CAUSAL_PAIRS) {
-    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, p.nq - 1 - t, false, -1);
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V, STRIDED>(p, lds, bh, p.nq - 1 - t, false, -1);
     return;
   }
   if (!CAUSAL) {
-    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, t, false, -1);
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V, STRIDED>(p, lds, bh, t, false, -1);
     return;
   }
   const int q_long = p.nq - 1 - t, q_short = t;
@@ -1114,7 +1147,7 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
   for (int k = 0; k < n_items; ++k) {
     // The second tile's copies reuse the LDS the first one's epilogue read.
     if (k > 0) lds_barrier();
-    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V>(p, lds, bh, k == 0 ? qa : qb,
+    attn_tile<S, IS_BF16, CAUSAL, OUT_F32, CONV_V, STRIDED>(p, lds, bh, k == 0 ? qa : qb,
                                                    S::OWN_STAGE && k > 0,
                                                    k + 1 < n_items ? qb : -1);
   }
@@ -1258,6 +1291,10 @@ constexpr int kPrepassBlocks = 8192;
 // N = 4096 (causal) and pays off from about twice that: kernel time grows
 // with N^2, the pass with N.
 constexpr int64_t kPrepassMinN = ATTN_CFG_PREPASS_MIN_N;
+// Largest row stride (elements) of a strided tensor the tuned kernels take:
+// a query tile of up to 256 rows then spans less than 2^31 bytes, the range
+// of a buffer descriptor and of the 32-bit copy offsets.
+constexpr int64_t kMaxRowStride = int64_t(1) << 21;
 
 // --------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.
@@ -1271,22 +1308,30 @@ struct Launch16 {
   unsigned threads;  // threads per workgroup
 };
 
+// Strided tensors: a kernel instance of its own, so the contiguous one keeps
+// its strides as compile-time constants; no first pass (bf16 V is converted
+// in LDS).
 template <class S, bool IS_BF16, bool CAUSAL>
-KernelFn pick16(bool out_f32, bool conv_v) {
+KernelFn pick16(bool out_f32, bool conv_v, bool strided) {
+  if (strided)
+    return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, IS_BF16, true>
+                   : attn_fwd_16<S, IS_BF16, CAUSAL, false, IS_BF16, true>;
   if (IS_BF16 && conv_v)
-    return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, IS_BF16>
-                   : attn_fwd_16<S, IS_BF16, CAUSAL, false, IS_BF16>;
-  return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, false>
-                 : attn_fwd_16<S, IS_BF16, CAUSAL, false, false>;
+    return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, IS_BF16, false>
+                   : attn_fwd_16<S, IS_BF16, CAUSAL, false, IS_BF16, false>;
+  return out_f32 ? attn_fwd_16<S, IS_BF16, CAUSAL, true, false, false>
+                 : attn_fwd_16<S, IS_BF16, CAUSAL, false, false, false>;
 }
 
 template <class S>
-Launch16 launch16(attn_dtype in, bool out_f32, bool causal, bool conv_v) {
+Launch16 launch16(attn_dtype in, bool out_f32, bool causal, bool conv_v, bool strided) {
   KernelFn fn;
   if (in == ATTN_BF16)
-    fn = causal ? pick16<S, true, true>(out_f32, conv_v) : pick16<S, true, false>(out_f32, conv_v);
+    fn = causal ? pick16<S, true, true>(out_f32, conv_v, strided)
+                : pick16<S, true, false>(out_f32, conv_v, strided);
   else
-    fn = causal ? pick16<S, false, true>(out_f32, false) : pick16<S, false, false>(out_f32, false);
+    fn = causal ? pick16<S, false, true>(out_f32, false, strided)
+                : pick16<S, false, false>(out_f32, false, strided);
   return Launch16{fn, S::BLOCK_M, (unsigned)S::THREADS};
 }
 
@@ -1328,23 +1373,23 @@ bool pick_wide(int64_t BH, int64_t N, bool causal, double narrow_unit_cost) {
 }
 
 Launch16 pick_launch16(int64_t d, int64_t BH, int64_t N, attn_dtype in, bool out_f32,
-                       bool causal, bool conv_v) {
+                       bool causal, bool conv_v, bool strided) {
   if (d == 128) {
 #if ATTN_FWD_D128_FORCED
     (void)BH;
-    return launch16<Tile16<128>>(in, out_f32, causal, conv_v);
+    return launch16<Tile16<128>>(in, out_f32, causal, conv_v, strided);
 #else
     if (pick_wide(BH, N, causal, 1.10))
-      return launch16<Shape16<128, 8, 64>>(in, out_f32, causal, conv_v);
-    return launch16<Shape16<128, 4, 32>>(in, out_f32, causal, conv_v);
+      return launch16<Shape16<128, 8, 64>>(in, out_f32, causal, conv_v, strided);
+    return launch16<Shape16<128, 4, 32>>(in, out_f32, causal, conv_v, strided);
 #endif
   }
 #if ATTN_FWD_D64_FORCED
-  return launch16<Tile16<64>>(in, out_f32, causal, conv_v);
+  return launch16<Tile16<64>>(in, out_f32, causal, conv_v, strided);
 #else
   if (pick_wide(BH, N, causal, 1.05))
-    return launch16<Shape16<64, 8, 128>>(in, out_f32, causal, conv_v);
-  return launch16<Shape16<64, 4, 64>>(in, out_f32, causal, conv_v);
+    return launch16<Shape16<64, 8, 128>>(in, out_f32, causal, conv_v, strided);
+  return launch16<Shape16<64, 4, 64>>(in, out_f32, causal, conv_v, strided);
 #endif
 }
 
@@ -1362,8 +1407,37 @@ thread_local int g_last_hip_error = 0;
 
 // The backward's translation unit reports launch errors through the same
 // per-thread slot that attn_last_hip_error() reads.
+extern "C" {
+static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse,
+                                 int64_t B, int64_t H, int64_t N, int64_t d, int causal,
+                                 float scale, attn_dtype in_dtype, attn_dtype out_dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const int64_t *strides);
+}
+
 namespace attn_internal {
 void set_last_hip_error(int e) { g_last_hip_error = e; }
+
+// Whether the tuned bf16/fp16 kernels take a strided problem of
+// attn_fwd_strided: equal query and key lengths, d of 64 or 128, and row
+// strides whose tiles fit a buffer descriptor's 32-bit range. st holds the
+// (batch, head, row) strides of q, k, v and o, validated by the caller.
+bool fwd16_takes_strided(int64_t Nq, int64_t Nk, int64_t d, attn_dtype in_dtype,
+                         const int64_t *st) {
+  if (Nq != Nk || (d != 64 && d != 128)) return false;
+  if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return false;
+  for (int t = 0; t < 4; ++t)
+    if (st[3 * t + 2] < d || st[3 * t + 2] > kMaxRowStride) return false;
+  return true;
+}
+
+attn_status fwd16_strided(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
+                          attn_dtype in_dtype, attn_dtype out_dtype, void *stream,
+                          const int64_t *st) {
+  return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
+                       stream, st);
+}
 }  // namespace attn_internal
 
 extern "C" {
@@ -1386,10 +1460,14 @@ const char *attn_status_string(attn_status s) {
   return "unknown status";
 }
 
+// strides: NULL for contiguous [B][H][N][d] tensors, else the (batch, head,
+// row) element strides of q, k, v and o, 12 values, already validated
+// (bf16/fp16 inputs, rows 16-byte aligned, row strides in [d, kMaxRowStride]).
 static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse,
                                  int64_t B, int64_t H, int64_t N, int64_t d, int causal,
                                  float scale, attn_dtype in_dtype, attn_dtype out_dtype,
-                                 void *workspace, size_t workspace_bytes, void *stream) {
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const int64_t *strides) {
   // Validation first: no HIP call happens before every argument is checked.
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
@@ -1404,14 +1482,15 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   // The first pass runs when the problem takes it and the workspace can hold
   // its output (16-byte aligned); otherwise the kernel converts V in LDS.
   // Both give the same bits.
-  const size_t need = prepass_bytes(B, H, N, d, in_dtype);
+  const size_t need = strides ? 0 : prepass_bytes(B, H, N, d, in_dtype);
   const bool prepass = need > 0 && workspace != nullptr && workspace_bytes >= need &&
                        (reinterpret_cast<uintptr_t>(workspace) & 15) == 0;
   const bool out_f32 = out_dtype == ATTN_F32;
   // The kernel, and its query rows and threads per workgroup.
   const bool f32_path = in_dtype == ATTN_F32;
   Launch16 l16 = {nullptr, 0, 0};
-  if (!f32_path) l16 = pick_launch16(d, B * H, N, in_dtype, out_f32, causal != 0, !prepass);
+  if (!f32_path)
+    l16 = pick_launch16(d, B * H, N, in_dtype, out_f32, causal != 0, !prepass, strides != nullptr);
   const int64_t block_m = f32_path ? kBlockM : l16.block_m;
   const unsigned threads = f32_path ? kThreads : l16.threads;
   const int64_t nq = (N + block_m - 1) / block_m;
@@ -1426,9 +1505,17 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   p.v_in = v;
   p.o = o;
   p.lse = lse;
+  const int64_t cont[3] = {H * N * d, N * d, d};
+  for (int i = 0; i < 3; ++i) {
+    p.qs[i] = strides ? strides[i] : cont[i];
+    p.ks[i] = strides ? strides[3 + i] : cont[i];
+    p.vs[i] = p.vis[i] = strides ? strides[6 + i] : cont[i];
+    p.os[i] = strides ? strides[9 + i] : cont[i];
+  }
   p.N = (int)N;
   p.nq = (int)nq;
   p.BH = (int)(B * H);
+  p.H = (int)H;
   // scale * log2(e) in double, rounded once; a zero scale becomes FLT_MIN so
   // masked scores (-inf) never meet a 0 factor.
   double qk = (double)scale * 1.4426950408889634;
@@ -1447,7 +1534,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
     void *cargs[] = {&src, &workspace, &n8};
     err = hipLaunchKernel(reinterpret_cast<const void *>(v_to_f16), dim3((unsigned)blocks),
                           dim3(256), cargs, 0, st);
-    p.v = workspace;
+    p.v = workspace;  // contiguous, like the caller's V (p.vis)
   }
   if (err == hipSuccess) {
     void *args[] = {&p};
@@ -1465,7 +1552,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                      int64_t H, int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
                      attn_dtype out_dtype, void *stream) {
   return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
-                       stream);
+                       stream, nullptr);
 }
 
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype) {
@@ -1477,7 +1564,7 @@ attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, fl
                         attn_dtype in_dtype, attn_dtype out_dtype, void *workspace,
                         size_t workspace_bytes, void *stream) {
   return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -75,8 +75,14 @@ KNOBS = {
                             workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
                             what="the backward's gradient stores with the non-temporal hint (1) "
                                  "or plain (0)"),
+    "strided_tuned": dict(macro="ATTN_CFG_STRIDED_TUNED", values=[1, 0], pass_="general",
+                          workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16",
+                                     "b4h16_n1024_d64_bf16"],
+                          what="strided self-attention at d = 64 or 128 (bf16/fp16) on the tuned "
+                               "kernels (1) or on the general kernel (0)"),
     "gen_o_nontemporal": dict(macro="ATTN_CFG_GEN_O_NONTEMPORAL", values=[0, 1], pass_="general",
                               workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                              base_defs=["-DATTN_CFG_STRIDED_TUNED=0"],
                               what="the general kernel's stores of O with the non-temporal hint "
                                    "(1) or plain (0)"),
     "fwd_lookahead": dict(macro="ATTN_CFG_LOOKAHEAD", values=[3, 2, 4], pass_="fwd",
@@ -105,33 +111,44 @@ KNOBS = {
                                "(3 spills)"),
     "gen_lookahead": dict(macro="ATTN_CFG_GEN_LOOKAHEAD", values=[2, 1, 3], pass_="general",
                           workloads=["b2h32_n4096_d128_bf16_causal", "b4h16_n1024_d64_bf16"],
+                          base_defs=["-DATTN_CFG_STRIDED_TUNED=0"],
                           what="MFMA steps by which the general kernel's LDS operand reads run "
                                "ahead"),
     "gen_tile_k": dict(macro="ATTN_CFG_GEN_TILE_K", values=["32@d128/64@d64", 32, 64, 128],
                        pass_="general",
                        workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
+                       base_defs=["-DATTN_CFG_STRIDED_TUNED=0"],
                        what="keys per step of the general-layout forward"),
 }
 
 
 def variant_name(knob, value):
-    return "default" if value == KNOBS[knob]["values"][0] else "%s_%s" % (knob, value)
+    """The shipped library for a knob's first value, unless the knob sets
+    base_defs (flags every variant of it is built with, e.g. to time the
+    general kernel on shapes the tuned kernels would otherwise take): then a
+    library of its own."""
+    if value == KNOBS[knob]["values"][0]:
+        return "%s_base" % knob if KNOBS[knob].get("base_defs") else "default"
+    return "%s_%s" % (knob, value)
 
 
 def variant_defs(knob, value):
     """-D flags of one value: a number for a one-macro knob, or "AxB" for a
-    knob over a pair of macros."""
+    knob over a pair of macros; plus the knob's base_defs."""
     macro = KNOBS[knob]["macro"]
+    base = list(KNOBS[knob].get("base_defs", []))
     if isinstance(value, str) and "x" not in value:
-        return []  # the library's own per-problem choice
+        return base  # the library's own per-problem choice
     if isinstance(macro, tuple):
-        return ["-D%s=%s" % (m, x) for m, x in zip(macro, str(value).split("x"))]
-    return ["-D%s=%d" % (macro, value)]
+        return base + ["-D%s=%s" % (m, x) for m, x in zip(macro, str(value).split("x"))]
+    return base + ["-D%s=%d" % (macro, value)]
 
 
 def _alternatives(knob):
-    """The values of a knob other than the shipped one (each a -D build)."""
-    return KNOBS[knob]["values"][1:]
+    """The values of a knob that need a build of their own: all but the
+    shipped one, and the first too when the knob sets base_defs."""
+    vals = KNOBS[knob]["values"]
+    return vals if KNOBS[knob].get("base_defs") else vals[1:]
 
 
 def lib_path(name):

@@ -112,10 +112,64 @@ def test_strided_layouts(dt, causal):
            scale, "strided %s causal=%s" % (dt, causal))
 
 
+TUNED_STRIDED = [
+    # (B, H, N, d, dtype, causal, out_dtype, V scale): tile shapes 8x64 and 4x32 (d=128),
+    # 8x128 and 4x64 (d=64); bf16 V beyond fp16's range (recomputed rows)
+    (2, 4, 1000, 128, "bf16", True, "f32", 1.0),
+    (1, 8, 2048, 128, "bf16", True, "f32", 1.0),
+    (4, 16, 1024, 64, "bf16", False, "in", 1.0),
+    (2, 3, 777, 64, "f16", False, "f32", 1.0),
+    (1, 2, 300, 128, "bf16", True, "f32", 1e5),
+]
+
+
+@pytest.mark.parametrize("case", TUNED_STRIDED, ids=lambda c: "B%dH%dN%dd%d_%s_c%d_%s_v%g" % c)
+def test_tuned_kernels_on_strided_views(case):
+    """attn_fwd_strided on self-attention at d = 64 or 128 runs the tuned
+    kernels with the tensors' own strides: Q and K as [B, N, H, d] views of
+    a fused projection, V a column slice of a wider [B, N, H, 2d] tensor (row
+    stride 2 H d), O into a [B, N, H, d] buffer. Only the addressing differs
+    from the contiguous call, so O and LSE must equal it bit for bit; the
+    contiguous call is itself held to the oracle on a few rows."""
+    B, H, N, d, dt, causal, out, vscale = case
+    print("case tuned strided", case, flush=True)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    odt = torch.float32 if out == "f32" else tdt
+    q, k, v = make_qkv(B, H, N, d, dt, 1.0, seed=36)
+    v = (v.float() * vscale).to(tdt)
+    scale = _scale(d)
+    qkv = torch.empty(B, N, 3, H, d, dtype=tdt, device=DEV)
+    wide = torch.zeros(B, N, H, 2 * d, dtype=tdt, device=DEV)
+    qs, ks = qkv[:, :, 0].transpose(1, 2), qkv[:, :, 1].transpose(1, 2)
+    vs = wide.transpose(1, 2)[..., d:]
+    qs.copy_(q.to(DEV)), ks.copy_(k.to(DEV)), vs.copy_(v.to(DEV))
+    assert not (qs.is_contiguous() or ks.is_contiguous() or vs.is_contiguous())
+    assert vs.stride(2) == 2 * H * d
+    obuf = torch.full((B, N, H, d), float("nan"), dtype=odt, device=DEV)
+    o_s, lse_s = binding.attn_fwd(qs, ks, vs, causal=causal, scale=scale, out_dtype=odt,
+                                  out=obuf.transpose(1, 2))
+    o_c, lse_c = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale,
+                                  out_dtype=odt)
+    torch.cuda.synchronize()
+    assert o_s.data_ptr() == obuf.data_ptr()
+    assert torch.isfinite(o_c).all()
+    assert torch.equal(o_s, o_c), "O: max diff %.3e" % float((o_s.float() - o_c.float()).abs().max())
+    assert torch.equal(lse_s, lse_c), "LSE differs"
+    rows = np.array([0, 1, N // 2, N - 1])
+    ro, rl = oracle.attn_oracle(q[:1, :1], k[:1, :1], v[:1, :1], causal=causal, scale=scale,
+                                rows=rows)
+    vmax = max(1.0, float(v[:1, :1].float().abs().max()))
+    err = np.abs(o_c[0, 0].cpu().double().numpy()[rows] - ro).max()
+    bar = (1e-2 + (2.0 ** -9 if out == "in" else 0.0) * np.abs(ro).max()) * vmax
+    assert err <= bar, "O rows: %.3e" % err
+    assert np.abs(lse_c[0, 0].cpu().double().numpy()[rows] - rl).max() <= 1e-3
+
+
 @pytest.mark.parametrize("d,dt,causal", [(128, "bf16", True), (64, "f16", False)])
 def test_general_kernel_on_fast_shapes(d, dt, causal):
-    """attn_fwd_strided on contiguous shapes the tuned kernels also take:
-    both within the forward's tolerance of the oracle."""
+    """attn_fwd_strided on contiguous shapes the tuned kernels take: it runs
+    them too, so its result equals attn_fwd's bit for bit; both within the
+    forward's tolerance of the oracle."""
     B, H, N = 2, 2, 513
     q, k, v = make_qkv(B, H, N, d, dt, 1.0, seed=34)
     scale = _scale(d)
@@ -124,6 +178,7 @@ def test_general_kernel_on_fast_shapes(d, dt, causal):
                                       out_dtype=torch.float32)
     o2, lse2 = binding.attn_fwd(qg, kg, vg, causal=causal, scale=scale, out_dtype=torch.float32)
     torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
     _check(o, lse, q, k, v, causal, scale, "general d=%d" % d)
     _check(o2, lse2, q, k, v, causal, scale, "tuned d=%d" % d)
 
