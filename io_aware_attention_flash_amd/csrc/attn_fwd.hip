@@ -67,7 +67,8 @@ struct FwdParams {
   // unit-stride); vs for v, vis for v_in. The fp32 kernel takes contiguous
   // tensors only.
   int64_t qs[3], ks[3], vs[3], vis[3], os[3];
-  int N;         // sequence length
+  int N;         // sequence length (query rows per head)
+  int Nk;        // keys per head: N, except for cross-attention (strided instances only)
   int nq;        // query tiles per (batch, head)
   int BH;        // batch * heads
   int H;         // heads
@@ -523,7 +524,7 @@ struct Pipe16 {
   uint16_t *lds;  // K stages 0..1, then V stages 0..1 (tile t in stage t % 2)
   const uint16_t *Kh, *Vh;
   LaneAddr<D> la;
-  int N, n_tiles, qrow, g, tid;
+  int N, Nq, n_tiles, qrow, g, tid;  // N: keys per head; Nq: query rows per head
   uint32_t lds_wave;  // LDS byte address of the buffer plus 1024 * wave (uniform)
   // Source offsets of this thread's 16 bytes in copy instruction c (kept in
   // registers: the descriptor's range check applies to them), and that of
@@ -555,9 +556,9 @@ struct Pipe16 {
     constexpr int TB = S::TILE_BYTES;
     dma16_to_lds(r, lds_wave + (kKStages + (t & 1)) * TB + c * S::INS_BYTES, v_dma[c]);
   }
-  // Copy of the workgroup's query tile (rows m0 ..; rows past N read as 0).
+  // Copy of the workgroup's query tile (rows m0 ..; rows past Nq read as 0).
   __device__ __forceinline__ void issue_q(const uint16_t *Qh, int m0) const {
-    const int rows = min(N - m0, S::BLOCK_M);
+    const int rows = min(Nq - m0, S::BLOCK_M);
     const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * (size_t)qrs);
     const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
@@ -833,7 +834,7 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, int bh, int 
                                                 RowState16<D> &st) {
   constexpr int NKC = D / 16, NCB = D / 32;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const int N = p.N;
+  const int N = STRIDED ? p.Nk : p.N;  // keys
   const size_t chead = (size_t)bh * (size_t)N * D;  // contiguous [B][H][N][D]
   const uint16_t *Kh = static_cast<const uint16_t *>(p.k) + (STRIDED ? head_off(p.ks, bh, p.H) : (int64_t)chead);
   const uint16_t *Vh =
@@ -945,7 +946,8 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
-  const int N = p.N;
+  const int N = p.N;                       // query rows
+  const int Nk = STRIDED ? p.Nk : N;       // keys
   const int m0 = qt * S::BLOCK_M;
   // Element offsets of this head and row strides: the tensors' own
   // (STRIDED), or those of contiguous [B][H][N][D] tensors, as constants.
@@ -960,7 +962,8 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   pp.krs = STRIDED ? (int)p.ks[2] : D;
   pp.vrs = STRIDED ? (int)p.vs[2] : D;
   pp.la = lane_addr<D>(lane);
-  pp.N = N;
+  pp.N = Nk;
+  pp.Nq = N;
   pp.g = g;
   pp.tid = tid;
   pp.qk = p.qk;
@@ -981,10 +984,10 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   // Key tiles to visit: for the workgroup (copies, barriers) and for this
   // wave (compute). Causal: only tiles holding some key <= the last row.
   // Tiles [0, nfw) need no mask for this wave.
-  const int n_all = (N + BN - 1) / BN;
+  const int n_all = (Nk + BN - 1) / BN;
   const int n_tiles = CAUSAL ? min(n_all, (m0 + S::BLOCK_M + BN - 1) / BN) : n_all;
   const int nw = CAUSAL ? min(n_all, (r0 + 32 + BN - 1) / BN) : n_all;
-  int nfw = N / BN;
+  int nfw = Nk / BN;
   if (CAUSAL) nfw = min(nfw, (r0 + 1) / BN);
   pp.n_tiles = n_tiles;
 
@@ -1018,9 +1021,9 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   f32x16 sa[S::NKB], sb[S::NKB];  // scores of the current / next tile
   qk_tile<S, IS_BF16>(sa, qf, pp.kstage(0), pp.la);
   if (nfw == 0)
-    softmax_max<S, CAUSAL, true>(st, sa, 0, N, pp.qrow, pp.qk, g);
+    softmax_max<S, CAUSAL, true>(st, sa, 0, Nk, pp.qrow, pp.qk, g);
   else
-    softmax_max<S, CAUSAL, false>(st, sa, 0, N, pp.qrow, pp.qk, g);
+    softmax_max<S, CAUSAL, false>(st, sa, 0, Nk, pp.qrow, pp.qk, g);
   wait_vmcnt<0>();  // K_1
   lds_barrier();
 
@@ -1412,19 +1415,22 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
                                  int64_t B, int64_t H, int64_t N, int64_t d, int causal,
                                  float scale, attn_dtype in_dtype, attn_dtype out_dtype,
                                  void *workspace, size_t workspace_bytes, void *stream,
-                                 const int64_t *strides);
+                                 const int64_t *strides, int64_t Nk);
 }
 
 namespace attn_internal {
 void set_last_hip_error(int e) { g_last_hip_error = e; }
 
 // Whether the tuned bf16/fp16 kernels take a strided problem of
-// attn_fwd_strided: equal query and key lengths, d of 64 or 128, and row
-// strides whose tiles fit a buffer descriptor's 32-bit range. st holds the
-// (batch, head, row) strides of q, k, v and o, validated by the caller.
-bool fwd16_takes_strided(int64_t Nq, int64_t Nk, int64_t d, attn_dtype in_dtype,
-                         const int64_t *st) {
-  if (Nq != Nk || (d != 64 && d != 128)) return false;
+// attn_fwd_strided (self- or cross-attention; the caller has checked that a
+// causal problem has equal query and key lengths): d of 128, or 64 with at
+// least 256 keys (with fewer, most of the tuned d=64 tile's 128-key stages
+// would be masked; the general kernel measured up to 14% faster there, the
+// tuned ones 2-11% faster from 256 keys on), and row strides whose tiles fit
+// a buffer descriptor's 32-bit range. st holds the (batch, head, row)
+// strides of q, k, v and o, validated by the caller.
+bool fwd16_takes_strided(int64_t Nk, int64_t d, attn_dtype in_dtype, const int64_t *st) {
+  if (d != 128 && !(d == 64 && Nk >= 256)) return false;
   if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return false;
   for (int t = 0; t < 4; ++t)
     if (st[3 * t + 2] < d || st[3 * t + 2] > kMaxRowStride) return false;
@@ -1432,11 +1438,11 @@ bool fwd16_takes_strided(int64_t Nq, int64_t Nk, int64_t d, attn_dtype in_dtype,
 }
 
 attn_status fwd16_strided(const void *q, const void *k, const void *v, void *o, float *lse,
-                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                          attn_dtype in_dtype, attn_dtype out_dtype, void *stream,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                          float scale, attn_dtype in_dtype, attn_dtype out_dtype, void *stream,
                           const int64_t *st) {
-  return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
-                       stream, st);
+  return attn_fwd_impl(q, k, v, o, lse, B, H, Nq, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
+                       stream, st, Nk);
 }
 }  // namespace attn_internal
 
@@ -1463,15 +1469,19 @@ const char *attn_status_string(attn_status s) {
 // strides: NULL for contiguous [B][H][N][d] tensors, else the (batch, head,
 // row) element strides of q, k, v and o, 12 values, already validated
 // (bf16/fp16 inputs, rows 16-byte aligned, row strides in [d, kMaxRowStride]).
+// Nk: keys per head; it may differ from N (query rows) only with strides and
+// without the causal mask.
 static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, void *o, float *lse,
                                  int64_t B, int64_t H, int64_t N, int64_t d, int causal,
                                  float scale, attn_dtype in_dtype, attn_dtype out_dtype,
                                  void *workspace, size_t workspace_bytes, void *stream,
-                                 const int64_t *strides) {
+                                 const int64_t *strides, int64_t Nk) {
   // Validation first: no HIP call happens before every argument is checked.
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
-  if (N > (int64_t(1) << 24) || B * H > (int64_t(1) << 24)) return ATTN_ERR_SHAPE;
+  if (B < 1 || H < 1 || N < 1 || Nk < 1) return ATTN_ERR_SHAPE;
+  if (N > (int64_t(1) << 24) || Nk > (int64_t(1) << 24) || B * H > (int64_t(1) << 24))
+    return ATTN_ERR_SHAPE;
+  if (Nk != N && (!strides || causal)) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
   const bool in_ok = in_dtype == ATTN_F32 || in_dtype == ATTN_F16 || in_dtype == ATTN_BF16;
   if (!in_ok) return ATTN_ERR_UNSUPPORTED;
@@ -1513,6 +1523,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
     p.os[i] = strides ? strides[9 + i] : cont[i];
   }
   p.N = (int)N;
+  p.Nk = (int)Nk;
   p.nq = (int)nq;
   p.BH = (int)(B * H);
   p.H = (int)H;
@@ -1552,7 +1563,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
                      int64_t H, int64_t N, int64_t d, int causal, float scale, attn_dtype in_dtype,
                      attn_dtype out_dtype, void *stream) {
   return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, nullptr, 0,
-                       stream, nullptr);
+                       stream, nullptr, N);
 }
 
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype) {
@@ -1564,7 +1575,7 @@ attn_status attn_fwd_ws(const void *q, const void *k, const void *v, void *o, fl
                         attn_dtype in_dtype, attn_dtype out_dtype, void *workspace,
                         size_t workspace_bytes, void *stream) {
   return attn_fwd_impl(q, k, v, o, lse, B, H, N, d, causal, scale, in_dtype, out_dtype, workspace,
-                       workspace_bytes, stream, nullptr);
+                       workspace_bytes, stream, nullptr, N);
 }
 
 }  // extern "C"

@@ -37,11 +37,10 @@ namespace attn_internal {
 void set_last_hip_error(int e);
 // The tuned bf16/fp16 forward (attn_fwd.hip) on strided tensors: whether it
 // takes a problem, and its launch.
-bool fwd16_takes_strided(int64_t Nq, int64_t Nk, int64_t d, attn_dtype in_dtype,
-                         const int64_t *st);
+bool fwd16_takes_strided(int64_t Nk, int64_t d, attn_dtype in_dtype, const int64_t *st);
 attn_status fwd16_strided(const void *q, const void *k, const void *v, void *o, float *lse,
-                          int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
-                          attn_dtype in_dtype, attn_dtype out_dtype, void *stream,
+                          int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                          float scale, attn_dtype in_dtype, attn_dtype out_dtype, void *stream,
                           const int64_t *st);
 }
 
@@ -78,8 +77,8 @@ constexpr int kTileKMax = 128;  // the largest key tile any build uses
 constexpr int kGenLookahead = ATTN_CFG_GEN_LOOKAHEAD;
 static_assert(kGenLookahead >= 1 && kGenLookahead <= 4, "lookahead range");
 constexpr float kRescaleLog2 = 8.0f;
-// Strided self-attention at d = 64 or 128 in bf16/fp16 on the tuned kernels
-// (1) or on this file's kernel (0).
+// Strided problems at d = 64 or 128 in bf16/fp16 on the tuned kernels (1)
+// or on this file's kernel (0).
 #ifndef ATTN_CFG_STRIDED_TUNED
 #define ATTN_CFG_STRIDED_TUNED 1
 #endif
@@ -709,15 +708,15 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
   if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileKMax >= (int64_t(1) << 31) ||
                                p.vs[2] * eb * kTileKMax >= (int64_t(1) << 31)))
     return ATTN_ERR_UNSUPPORTED;
-  // Self-attention at d = 64 or 128 in bf16/fp16 runs on the tuned kernels,
-  // which read and write rows through the same strides.
+  // d = 128 (or 64 with enough keys) in bf16/fp16 runs on the tuned
+  // kernels, which read and write rows through the same strides.
   if (ATTN_CFG_STRIDED_TUNED) {
     int64_t st[12];
     for (int i = 0; i < 3; ++i)
       st[i] = p.qs[i], st[3 + i] = p.ks[i], st[6 + i] = p.vs[i], st[9 + i] = p.os[i];
-    if (attn_internal::fwd16_takes_strided(Nq, Nk, d, in_dtype, st))
-      return attn_internal::fwd16_strided(q, k, v, o, lse, B, H, Nq, d, causal, scale, in_dtype,
-                                          out_dtype, stream, st);
+    if (attn_internal::fwd16_takes_strided(Nk, d, in_dtype, st))
+      return attn_internal::fwd16_strided(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale,
+                                          in_dtype, out_dtype, stream, st);
   }
   const int64_t nq = (Nq + kBlockM - 1) / kBlockM;
   const int64_t grid = nq * B * H;

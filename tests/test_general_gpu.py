@@ -54,6 +54,10 @@ CROSS = [
     # d <= 64 takes 128-key tiles up to 1024 keys and 64-key tiles past that
     (1, 2, 100, 1024, 64, "bf16", 1.0), (1, 2, 100, 1025, 64, "f16", 1.0),
     (1, 1, 70, 1500, 48, "bf16", 2.0),
+    # d = 64 / 128 in bf16/fp16 run on the tuned kernels: few keys, one query, many query
+    # tiles against few keys, a ragged key tail
+    (1, 2, 257, 1, 128, "bf16", 1.0), (1, 3, 1, 5000, 128, "bf16", 1.0),
+    (2, 2, 700, 129, 64, "f16", 1.0), (1, 4, 2048, 333, 128, "bf16", 1.0),
 ]
 
 
