@@ -67,6 +67,8 @@ struct FwdParams {
   // unit-stride); vs for v, vis for v_in. The fp32 kernel takes contiguous
   // tensors only.
   int64_t qs[3], ks[3], vs[3], vis[3], os[3];
+  int d;         // head dimension of the tensors: D, or (strided instances) a multiple of 8
+                 // below it, whose columns d .. D-1 read as zeros and are not stored
   int N;         // sequence length (query rows per head)
   int Nk;        // keys per head: N, except for cross-attention (strided instances only)
   int nq;        // query tiles per (batch, head)
@@ -306,13 +308,15 @@ constexpr int kBufferFlags = 0x00020000;
 // readfirstlane says so to the compiler, which keeps the words in scalar
 // registers.
 template <class S>
-__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N, int rs) {
-  constexpr int BN = S::BN, D = S::D;
+__device__ __forceinline__ u32x4 tile_rsrc(const uint16_t *head, int t, int n_tiles, int N, int rs,
+                                           int dcol) {
+  constexpr int BN = S::BN;
   const int keys = t < n_tiles ? min(N - t * BN, BN) : 0;
   const uint16_t *base = keys > 0 ? head + (size_t)t * BN * (size_t)rs : head;
-  // the last key's row ends D elements after its start: (keys - 1) rows of
-  // rs elements and one of D (keys * D * 2 bytes for contiguous rows)
-  const uint32_t bytes = (uint32_t)(keys * rs * 2 - (keys > 0 ? (rs - D) * 2 : 0));
+  // the last key's row ends dcol elements after its start: (keys - 1) rows
+  // of rs elements and one of dcol (keys * D * 2 bytes for contiguous rows);
+  // rows at or past `keys` start at or past that end (rs >= dcol)
+  const uint32_t bytes = (uint32_t)(keys * rs * 2 - (keys > 0 ? (rs - dcol) * 2 : 0));
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return u32x4{(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,  // stride 0
@@ -347,12 +351,18 @@ __device__ __forceinline__ void dma16_to_lds_nt(u32x4 rsrc, uint32_t lds_byte, u
 // lane offset is that of c = 0 plus c * (THREADS / CPR) rows of rs elements.
 // The offset stays in a VGPR (the descriptor's range check applies to it,
 // not to an SGPR offset).
-template <int D, bool IS_V>
-__device__ __forceinline__ uint32_t dma_offset(int tid, int rs) {
+// With PAD, a lane whose 16-byte piece starts at or past column dcol gets
+// kOutOfRange instead: every copy of it reads zeros (the offsets of later
+// instructions add less than 2^30 to it, so they stay out of range too).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+template <int D, bool IS_V, bool PAD>
+__device__ __forceinline__ uint32_t dma_offset(int tid, int rs, int dcol) {
   constexpr int CPR = D / 8;
   const int row0 = tid / CPR;
   const int swz = IS_V ? swz_v<D>(row0) : swz_k<D>(row0);
-  return (uint32_t)(row0 * rs * 2) + (((tid % CPR) ^ swz) << 4);
+  const int lc = (tid % CPR) ^ swz;  // logical 16-byte chunk of the row
+  if (PAD && lc * 8 >= dcol) return kOutOfRange;
+  return (uint32_t)(row0 * rs * 2) + (lc << 4);
 }
 // Wait until at most N vector-memory instructions of this wave are
 // outstanding (they retire in order).
@@ -531,6 +541,7 @@ struct Pipe16 {
   // the query tile's first copy instruction.
   uint32_t k_dma[S::DMA_INS], v_dma[S::DMA_INS], q_dma0;
   int qrs, krs, vrs;  // row strides (elements) of Q, K and V
+  int dcol;           // columns of the tensors (D, or fewer for strided instances)
   float qk;
 
   __device__ __forceinline__ uint16_t *kstage(int par) const {
@@ -545,8 +556,12 @@ struct Pipe16 {
   // V_{j+1}, then K_{j+2}, into the stages V_{j-1} and K_j left (free since
   // the barrier that ended iteration j-1); a late step waits for V_{j+1}
   // and converts it (bf16); the iteration ends by waiting for K_{j+2}.
-  __device__ __forceinline__ u32x4 k_rsrc(int t) const { return tile_rsrc<S>(Kh, t, n_tiles, N, krs); }
-  __device__ __forceinline__ u32x4 v_rsrc(int t) const { return tile_rsrc<S>(Vh, t, n_tiles, N, vrs); }
+  __device__ __forceinline__ u32x4 k_rsrc(int t) const {
+    return tile_rsrc<S>(Kh, t, n_tiles, N, krs, dcol);
+  }
+  __device__ __forceinline__ u32x4 v_rsrc(int t) const {
+    return tile_rsrc<S>(Vh, t, n_tiles, N, vrs, dcol);
+  }
   // Instruction c of the copy of K_t / V_t (descriptor r).
   __device__ __forceinline__ void copy_k(u32x4 r, int t, int c) const {
     constexpr int TB = S::TILE_BYTES;
@@ -562,7 +577,7 @@ struct Pipe16 {
     const uint64_t a = reinterpret_cast<uint64_t>(Qh + (size_t)m0 * (size_t)qrs);
     const u32x4 r = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) & 0xFFFFu,
-                     (uint32_t)__builtin_amdgcn_readfirstlane(((rows - 1) * qrs + D) * 2),
+                     (uint32_t)__builtin_amdgcn_readfirstlane(((rows - 1) * qrs + dcol) * 2),
                      (uint32_t)kBufferFlags};
     constexpr int RPI = S::THREADS / S::CPR;  // rows per copy instruction
 #pragma unroll
@@ -840,6 +855,7 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, int bh, int 
   const uint16_t *Vh =
       static_cast<const uint16_t *>(p.v_in) + (STRIDED ? head_off(p.vis, bh, p.H) : (int64_t)chead);
   const int64_t krs = STRIDED ? p.ks[2] : D, vrs = STRIDED ? p.vis[2] : D;
+  const int dcol = STRIDED ? p.d : D;  // columns past dcol read as zeros
   const int kend = CAUSAL ? min(N, r0 + 32) : N;
   const float qk = p.qk, neg_m = st.neg_m;
   float l = 0.f;
@@ -853,8 +869,13 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, int bh, int 
     f32x16 sc = f32x16{};
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      u32x4 kf = *reinterpret_cast<const u32x4 *>(krow + 16 * kc);
-      if (key >= N) kf = u32x4{0, 0, 0, 0};
+      u32x4 kf = u32x4{0, 0, 0, 0};
+      if (STRIDED) {  // no load past column dcol: it may lie past the tensor
+        if (key < N && 16 * kc + 8 * g < dcol) kf = *reinterpret_cast<const u32x4 *>(krow + 16 * kc);
+      } else {
+        kf = *reinterpret_cast<const u32x4 *>(krow + 16 * kc);
+        if (key >= N) kf = u32x4{0, 0, 0, 0};
+      }
       sc = mfma_qk<true>(kf, qf[kc], sc);
     }
     // weights, rounded to bf16 and packed as the P^T operands of the two
@@ -884,7 +905,7 @@ __device__ __forceinline__ float redo_rows_bf16(const FwdParams &p, int bh, int 
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           const int kk = k0 + 16 * t + 8 * (x >> 2) + 4 * g + (x & 3);
-          vv[x] = kk < N ? Vh[(int64_t)kk * vrs + 32 * cb + l32] : 0u;
+          vv[x] = kk < N && 32 * cb + l32 < dcol ? Vh[(int64_t)kk * vrs + 32 * cb + l32] : 0u;
         }
         const u32x4 a = {vv[0] | (vv[1] << 16), vv[2] | (vv[3] << 16), vv[4] | (vv[5] << 16),
                          vv[6] | (vv[7] << 16)};
@@ -961,6 +982,7 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   pp.qrs = STRIDED ? (int)p.qs[2] : D;
   pp.krs = STRIDED ? (int)p.ks[2] : D;
   pp.vrs = STRIDED ? (int)p.vs[2] : D;
+  pp.dcol = STRIDED ? p.d : D;
   pp.la = lane_addr<D>(lane);
   pp.N = Nk;
   pp.Nq = N;
@@ -971,10 +993,10 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
   constexpr int RPI = S::THREADS / S::CPR;  // tile rows per copy instruction
 #pragma unroll
   for (int c = 0; c < S::DMA_INS; ++c) {
-    pp.k_dma[c] = dma_offset<D, false>(tid, pp.krs) + (uint32_t)(c * RPI * pp.krs * 2);
-    pp.v_dma[c] = dma_offset<D, true>(tid, pp.vrs) + (uint32_t)(c * RPI * pp.vrs * 2);
+    pp.k_dma[c] = dma_offset<D, false, STRIDED>(tid, pp.krs, pp.dcol) + (uint32_t)(c * RPI * pp.krs * 2);
+    pp.v_dma[c] = dma_offset<D, true, STRIDED>(tid, pp.vrs, pp.dcol) + (uint32_t)(c * RPI * pp.vrs * 2);
   }
-  pp.q_dma0 = dma_offset<D, false>(tid, pp.qrs);
+  pp.q_dma0 = dma_offset<D, false, STRIDED>(tid, pp.qrs, pp.dcol);
   // This lane's query row. Rows past N read zeros (the query tile's copy
   // descriptor is cut at N) and are never stored.
   const int r0 = m0 + wave * 32;  // first row of this wave
@@ -1099,7 +1121,8 @@ __device__ __forceinline__ void attn_tile(const FwdParams &p, uint16_t *lds, int
       const int row = k * OS::RPI + lane / OS::CPR, c = lane % OS::CPR;
       const u32x4 val =
           *reinterpret_cast<const u32x4 *>(stage + row * OS::ROWB + ((c ^ OS::swz(row)) << 4));
-      if (r0 + row < N)
+      // strided instances: 16-byte pieces at or past column d are not stored
+      if (r0 + row < N && (!STRIDED || (ps * OS::ROWB + c * 16) / OS::E < pp.dcol))
       {
         u32x4 *dst = reinterpret_cast<u32x4 *>(obase + (int64_t)row * ors * OS::E + ps * OS::ROWB + c * 16);
         if (ATTN_CFG_O_NONTEMPORAL) __builtin_nontemporal_store(val, dst); else *dst = val;
@@ -1423,14 +1446,15 @@ void set_last_hip_error(int e) { g_last_hip_error = e; }
 
 // Whether the tuned bf16/fp16 kernels take a strided problem of
 // attn_fwd_strided (self- or cross-attention; the caller has checked that a
-// causal problem has equal query and key lengths): d of 128, or 64 with at
-// least 256 keys (with fewer, most of the tuned d=64 tile's 128-key stages
+// causal problem has equal query and key lengths, and that d is a multiple
+// of 8 up to 128): computed at D = 128 (d > 64) always, at D = 64 with at
+// least 256 keys (with fewer, most of the tuned D=64 tile's 128-key stages
 // would be masked; the general kernel measured up to 14% faster there, the
 // tuned ones 2-11% faster from 256 keys on), and row strides whose tiles fit
 // a buffer descriptor's 32-bit range. st holds the (batch, head, row)
 // strides of q, k, v and o, validated by the caller.
 bool fwd16_takes_strided(int64_t Nk, int64_t d, attn_dtype in_dtype, const int64_t *st) {
-  if (d != 128 && !(d == 64 && Nk >= 256)) return false;
+  if (d <= 64 && Nk < 256) return false;
   if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return false;
   for (int t = 0; t < 4; ++t)
     if (st[3 * t + 2] < d || st[3 * t + 2] > kMaxRowStride) return false;
@@ -1482,7 +1506,12 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   if (N > (int64_t(1) << 24) || Nk > (int64_t(1) << 24) || B * H > (int64_t(1) << 24))
     return ATTN_ERR_SHAPE;
   if (Nk != N && (!strides || causal)) return ATTN_ERR_SHAPE;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // Contiguous tensors: d = 64 or 128. Strided ones: a multiple of 8 up to
+  // 128, computed at D = 64 or 128 with zero columns.
+  if (strides ? (d < 8 || d > 128 || d % 8 != 0) : (d != 64 && d != 128))
+    return ATTN_ERR_UNSUPPORTED;
+  const int64_t D = d <= 64 ? 64 : 128;
+  if (strides && in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return ATTN_ERR_UNSUPPORTED;
   const bool in_ok = in_dtype == ATTN_F32 || in_dtype == ATTN_F16 || in_dtype == ATTN_BF16;
   if (!in_ok) return ATTN_ERR_UNSUPPORTED;
   if (in_dtype == ATTN_F32 && out_dtype != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
@@ -1500,7 +1529,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   const bool f32_path = in_dtype == ATTN_F32;
   Launch16 l16 = {nullptr, 0, 0};
   if (!f32_path)
-    l16 = pick_launch16(d, B * H, N, in_dtype, out_f32, causal != 0, !prepass, strides != nullptr);
+    l16 = pick_launch16(D, B * H, N, in_dtype, out_f32, causal != 0, !prepass, strides != nullptr);
   const int64_t block_m = f32_path ? kBlockM : l16.block_m;
   const unsigned threads = f32_path ? kThreads : l16.threads;
   const int64_t nq = (N + block_m - 1) / block_m;
@@ -1522,6 +1551,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
     p.vs[i] = p.vis[i] = strides ? strides[6 + i] : cont[i];
     p.os[i] = strides ? strides[9 + i] : cont[i];
   }
+  p.d = (int)d;
   p.N = (int)N;
   p.Nk = (int)Nk;
   p.nq = (int)nq;

@@ -169,6 +169,42 @@ def test_tuned_kernels_on_strided_views(case):
     assert np.abs(lse_c[0, 0].cpu().double().numpy()[rows] - rl).max() <= 1e-3
 
 
+PADDED = [
+    # (B, H, Nq, Nk, d, dtype, causal): computed at D = 128 (d > 64) or 64 (Nk >= 256)
+    (2, 3, 1000, 1000, 80, "bf16", True), (1, 4, 700, 700, 96, "f16", False),
+    (2, 2, 513, 513, 112, "bf16", True), (1, 3, 600, 600, 40, "bf16", True),
+    (2, 2, 300, 1100, 24, "f16", False), (1, 2, 77, 2000, 72, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", PADDED, ids=lambda c: "B%dH%dNq%dNk%dd%d_%s_c%d" % c)
+def test_tuned_kernels_on_padded_head_dims(case):
+    """Head dims other than 64 and 128 on the tuned kernels (strided
+    instances): the columns d .. D-1 are read as zeros, so the result equals,
+    bit for bit, the contiguous call on the same tensors zero-padded to D
+    columns (O's first d columns, LSE); the padded call is held to the
+    oracle on a few rows."""
+    B, H, Nq, Nk, d, dt, causal = case
+    print("case padded", case, flush=True)
+    D = 64 if d <= 64 else 128
+    q, k, v = _qkv(B, H, Nq, Nk, d, dt, 1.0, seed=37)
+    scale = _scale(d)
+    o, lse = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), causal=causal, scale=scale,
+                              out_dtype=torch.float32)
+    pad = lambda x: torch.nn.functional.pad(x, (0, D - d)).to(DEV)
+    if Nq == Nk:
+        o_p, lse_p = binding.attn_fwd(pad(q), pad(k), pad(v), causal=causal, scale=scale,
+                                      out_dtype=torch.float32)
+    else:  # the contiguous tuned call needs Nq == Nk: the strided entry on padded tensors
+        o_p, lse_p = binding.attn_fwd_general(pad(q), pad(k), pad(v), causal=causal, scale=scale,
+                                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_p[..., :d]), "O: max diff %.3e" % float((o - o_p[..., :d]).abs().max())
+    assert torch.equal(lse, lse_p)
+    assert not o_p[..., d:].abs().max() > 0
+    _check(o, lse, q, k, v, causal, scale, "padded %s" % (case,))
+
+
 @pytest.mark.parametrize("d,dt,causal", [(128, "bf16", True), (64, "f16", False)])
 def test_general_kernel_on_fast_shapes(d, dt, causal):
     """attn_fwd_strided on contiguous shapes the tuned kernels take: it runs
