@@ -169,6 +169,49 @@ def test_tuned_kernels_on_strided_views(case):
     assert np.abs(lse_c[0, 0].cpu().double().numpy()[rows] - rl).max() <= 1e-3
 
 
+def test_tuned_strided_full_headline_shape():
+    """The strided instance at the full B2 H32 N4096 d128 causal bf16 shape on
+    [B, N, H, d] views (what bench.py --pass fwd_general times): every element
+    of O and LSE equals the contiguous call's."""
+    B, H, N, d = 2, 32, 4096, 128
+    q, k, v = (x.to(DEV) for x in make_qkv(B, H, N, d, "bf16", 1.0, seed=0))
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    scale = _scale(d)
+    obuf = torch.empty(B, N, H, d, dtype=torch.float32, device=DEV)
+    o_s, lse_s = binding.attn_fwd(qs, ks, vs, causal=True, scale=scale, out_dtype=torch.float32,
+                                  out=obuf.transpose(1, 2))
+    o_c, lse_c = binding.attn_fwd(q, k, v, causal=True, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_c) and torch.equal(lse_s, lse_c)
+
+
+def test_tuned_cross_attention_large():
+    """Cross-attention at B2 H16 Nq 4096 Nk 1024 d128 bf16 on the tuned
+    kernels: sampled rows of every head against the oracle (the forward's
+    bar), properties over every output."""
+    B, H, Nq, Nk, d = 2, 16, 4096, 1024, 128
+    q, k, v = _qkv(B, H, Nq, Nk, d, "bf16", 1.0, seed=38)
+    scale = _scale(d)
+    o, lse = binding.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale,
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    oc, lc = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.all(np.isfinite(oc)) and np.all(np.isfinite(lc))
+    vmin = v.double().numpy().min(axis=2, keepdims=True)
+    vmax = v.double().numpy().max(axis=2, keepdims=True)
+    assert np.all(oc >= vmin - 1e-6) and np.all(oc <= vmax + 1e-6)
+    rng = np.random.default_rng(38)
+    rows_in_head = np.unique(np.concatenate([[0, 1, 255, 256, Nq - 1], rng.integers(0, Nq, 12)]))
+    rows = np.concatenate([bh * Nq + rows_in_head for bh in range(B * H)])
+    ro, rl = oracle.attn_oracle(q, k, v, causal=False, scale=scale, rows=rows)
+    go = oc.reshape(B * H * Nq, d)[rows]
+    gl = lc.reshape(B * H * Nq)[rows]
+    err, lerr = np.abs(go - ro), np.abs(gl - rl)
+    print("cross large: O max %.3e mean %.3e | LSE max %.3e over %d rows" % (
+        err.max(), err.mean(), lerr.max(), len(rows)), flush=True)
+    assert err.max() <= O_MAX and err.mean() <= O_MEAN and lerr.max() <= LSE_MAX
+
+
 PADDED = [
     # (B, H, Nq, Nk, d, dtype, causal): computed at D = 128 (d > 64) or 64 (Nk >= 256)
     (2, 3, 1000, 1000, 80, "bf16", True), (1, 4, 700, 700, 96, "f16", False),
