@@ -38,3 +38,19 @@ def test_fake_outputs_are_contiguous_for_strided_inputs():
         grads = torch.ops.io_aware_attention_flash.bwd(q, q, q, o, lse, q, False, 0.125)
         for g in grads:
             assert g.shape == q.shape and g.is_contiguous()
+
+
+def test_export_sees_the_operator():
+    """torch.export traces a module that calls flash_attn_func into a graph
+    holding the registered operator (the fake implementation gives the shapes;
+    nothing runs on a GPU)."""
+    class Attn(torch.nn.Module):
+        def forward(self, q, k, v):
+            return pkg.flash_attn_func(q, k, v, causal=True)
+
+    q = torch.randn(1, 2, 16, 64, dtype=torch.bfloat16)
+    ep = torch.export.export(Attn(), (q, q, q))
+    targets = [str(n.target) for n in ep.graph.nodes if n.op == "call_function"]
+    assert any("io_aware_attention_flash.fwd" in t for t in targets), targets
+    out = [n for n in ep.graph.nodes if n.op == "output"][0]
+    assert out is not None
