@@ -82,6 +82,22 @@ __device__ __forceinline__ float row_reduce(float v, float *red, int wave) {
 template <int WPR>
 constexpr int rows_threads() { return WPR == 1 ? 256 : 64 * WPR; }
 
+// Each row of x is read once and each row of y written once by the one-pass
+// kernel: with the non-temporal hint (1) on those 16-byte loads and stores,
+// or plain (0).
+#ifndef ATTN_CFG_SM_NONTEMPORAL
+#define ATTN_CFG_SM_NONTEMPORAL 1
+#endif
+template <typename V>
+__device__ __forceinline__ V load_once(const V *p) {
+  if (ATTN_CFG_SM_NONTEMPORAL) return __builtin_nontemporal_load(p);
+  return *p;
+}
+template <typename V>
+__device__ __forceinline__ void store_once(V v, V *p) {
+  if (ATTN_CFG_SM_NONTEMPORAL) __builtin_nontemporal_store(v, p); else *p = v;
+}
+
 // Rows held in registers: VPL values per lane, WPR waves per row (64 * WPR
 // lanes), N <= 64 * WPR * VPL. VEC: each lane moves 16-byte pieces (CH
 // values), piece k of lane t at columns (k * 64 * WPR + t) * CH; otherwise
@@ -110,7 +126,7 @@ __global__ __launch_bounds__(rows_threads<WPR>()) void softmax_rows(SmParams p) 
     for (int k = 0; k < NP; ++k) {
       const int c0 = (k * T + t) * CH;
       union { u32x4 w; TIN e[CH]; } u;
-      u.w = live && c0 < N ? *reinterpret_cast<const u32x4 *>(xr + c0) : u32x4{0, 0, 0, 0};
+      u.w = live && c0 < N ? load_once(reinterpret_cast<const u32x4 *>(xr + c0)) : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int e = 0; e < CH; ++e) v[k * CH + e] = live && c0 < N ? to_f32<TIN>(u.e[e]) : -INFINITY;
     }
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(rows_threads<WPR>()) void softmax_rows(SmParams p) 
         union { u32x4 w; TOUT e[OCH]; } u;
 #pragma unroll
         for (int e = 0; e < OCH; ++e) u.e[e] = from_f32<TOUT>(v[k * CH + s * OCH + e] * inv);
-        *reinterpret_cast<u32x4 *>(yr + c0 + s * OCH) = u.w;
+        store_once(u.w, reinterpret_cast<u32x4 *>(yr + c0 + s * OCH));
       }
     }
   } else {
