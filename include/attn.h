@@ -285,13 +285,14 @@ attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const 
  * causal     : requires Nq == Nk (else ATTN_ERR_SHAPE).
  * d          : a multiple of 8 in [8, 128] (else ATTN_ERR_UNSUPPORTED).
  * Other arguments, dtype pairs, precision, errors and ownership are those of
- * attn_fwd. bf16/fp16 problems with d > 64, or d <= 64 and Nk >= 256, with
- * row strides of at most 2^21 elements run on attn_fwd's kernels (at 64 or
- * 128 columns, those past d read as zeros and not stored), reading and
- * writing through the strides; the result then equals attn_fwd's on the
- * same values zero-padded to 64 or 128 columns, bit for bit. Every other
- * problem runs on a separate, simpler kernel, whose results equal attn_fwd's
- * within the forward's tolerance, not bitwise.
+ * attn_fwd. bf16/fp16 problems with row strides of at most 2^21 elements
+ * run on attn_fwd's kernels (at 64 or 128 columns, those past d read as
+ * zeros and not stored), reading and writing through the strides; for
+ * self-attention the result equals attn_fwd's on the same values
+ * zero-padded to 64 or 128 columns, bit for bit. fp32 problems (and
+ * bf16/fp16 ones with longer row strides) run on a separate, simpler
+ * kernel, whose results equal attn_fwd's within the forward's tolerance,
+ * not bitwise.
  */
 attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void *k,
                              const int64_t *k_strides, const void *v, const int64_t *v_strides,

@@ -1398,7 +1398,7 @@ bool pick_wide(int64_t BH, int64_t N, bool causal, double narrow_unit_cost) {
   return tile_cost(u8, 1, 1.0) <= tile_cost(u4, 2, narrow_unit_cost);
 }
 
-Launch16 pick_launch16(int64_t d, int64_t BH, int64_t N, attn_dtype in, bool out_f32,
+Launch16 pick_launch16(int64_t d, int64_t BH, int64_t N, int64_t Nk, attn_dtype in, bool out_f32,
                        bool causal, bool conv_v, bool strided) {
   if (d == 128) {
 #if ATTN_FWD_D128_FORCED
@@ -1411,9 +1411,12 @@ Launch16 pick_launch16(int64_t d, int64_t BH, int64_t N, attn_dtype in, bool out
 #endif
   }
 #if ATTN_FWD_D64_FORCED
+  (void)Nk;
   return launch16<Tile16<64>>(in, out_f32, causal, conv_v, strided);
 #else
-  if (pick_wide(BH, N, causal, 1.05))
+  // With fewer than 256 keys most of the 8-wave tile's 128-key stages would
+  // be masked: the 64-key tile (measured 17-27% faster at 77-255 keys).
+  if (Nk >= 256 && pick_wide(BH, N, causal, 1.05))
     return launch16<Shape16<64, 8, 128>>(in, out_f32, causal, conv_v, strided);
   return launch16<Shape16<64, 4, 64>>(in, out_f32, causal, conv_v, strided);
 #endif
@@ -1447,14 +1450,11 @@ void set_last_hip_error(int e) { g_last_hip_error = e; }
 // Whether the tuned bf16/fp16 kernels take a strided problem of
 // attn_fwd_strided (self- or cross-attention; the caller has checked that a
 // causal problem has equal query and key lengths, and that d is a multiple
-// of 8 up to 128): computed at D = 128 (d > 64) always, at D = 64 with at
-// least 256 keys (with fewer, most of the tuned D=64 tile's 128-key stages
-// would be masked; the general kernel measured up to 14% faster there, the
-// tuned ones 2-11% faster from 256 keys on), and row strides whose tiles fit
-// a buffer descriptor's 32-bit range. st holds the (batch, head, row)
-// strides of q, k, v and o, validated by the caller.
+// of 8 up to 128): bf16/fp16 inputs, and row strides whose tiles fit a
+// buffer descriptor's 32-bit range. st holds the (batch, head, row) strides
+// of q, k, v and o, validated by the caller.
 bool fwd16_takes_strided(int64_t Nk, int64_t d, attn_dtype in_dtype, const int64_t *st) {
-  if (d <= 64 && Nk < 256) return false;
+  (void)Nk, (void)d;
   if (in_dtype != ATTN_BF16 && in_dtype != ATTN_F16) return false;
   for (int t = 0; t < 4; ++t)
     if (st[3 * t + 2] < d || st[3 * t + 2] > kMaxRowStride) return false;
@@ -1529,7 +1529,7 @@ static attn_status attn_fwd_impl(const void *q, const void *k, const void *v, vo
   const bool f32_path = in_dtype == ATTN_F32;
   Launch16 l16 = {nullptr, 0, 0};
   if (!f32_path)
-    l16 = pick_launch16(D, B * H, N, in_dtype, out_f32, causal != 0, !prepass, strides != nullptr);
+    l16 = pick_launch16(D, B * H, N, Nk, in_dtype, out_f32, causal != 0, !prepass, strides != nullptr);
   const int64_t block_m = f32_path ? kBlockM : l16.block_m;
   const unsigned threads = f32_path ? kThreads : l16.threads;
   const int64_t nq = (N + block_m - 1) / block_m;

@@ -77,8 +77,8 @@ constexpr int kTileKMax = 128;  // the largest key tile any build uses
 constexpr int kGenLookahead = ATTN_CFG_GEN_LOOKAHEAD;
 static_assert(kGenLookahead >= 1 && kGenLookahead <= 4, "lookahead range");
 constexpr float kRescaleLog2 = 8.0f;
-// Strided problems at d = 64 or 128 in bf16/fp16 on the tuned kernels (1)
-// or on this file's kernel (0).
+// Strided bf16/fp16 problems on the tuned kernels (1) or on this file's
+// kernel (0).
 #ifndef ATTN_CFG_STRIDED_TUNED
 #define ATTN_CFG_STRIDED_TUNED 1
 #endif
@@ -708,8 +708,8 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
   if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileKMax >= (int64_t(1) << 31) ||
                                p.vs[2] * eb * kTileKMax >= (int64_t(1) << 31)))
     return ATTN_ERR_UNSUPPORTED;
-  // d = 128 (or 64 with enough keys) in bf16/fp16 runs on the tuned
-  // kernels, which read and write rows through the same strides.
+  // bf16/fp16 runs on the tuned kernels, which read and write rows through
+  // the same strides.
   if (ATTN_CFG_STRIDED_TUNED) {
     int64_t st[12];
     for (int i = 0; i < 3; ++i)
