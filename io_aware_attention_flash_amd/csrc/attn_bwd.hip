@@ -345,6 +345,32 @@ __device__ __forceinline__ void unpack8(const u32x4 &w, float (&x)[8]) {
   }
 }
 
+// sum_c dO_c O_c over the columns 16kc + 8g .. +7 (kc < NKC, below d) of one
+// row: dO from the packed operands df, O (element type OT) read at ro. All
+// loads are issued before the first product, so their latencies overlap.
+template <int OT, int NKC, bool IS_BF16>
+__device__ __forceinline__ float row_dot_o(const void *o, int64_t ro, const u32x4 *df, int g, int d) {
+  float of[NKC][8];
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    if (16 * kc + 8 * g < d) {
+      load8<OT, ATTN_CFG_BWD_O_NONTEMPORAL>(o, ro + 16 * kc, of[kc]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) of[kc][c] = 0.f;
+    }
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < NKC; ++kc) {
+    float dof[8];
+    unpack8<IS_BF16>(df[kc], dof);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc += dof[c] * of[kc][c];
+  }
+  return acc;
+}
+
 template <int D, int IN, bool O_F32>
 __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
@@ -621,16 +647,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq(BwdParams p) {
   float dd = 0.f, l2 = 0.f;
   if (my_q < Nq) {
     const int64_t ro = head_off(p.os, bh, p.H) + (int64_t)my_q * p.os[2] + 8 * g;
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      if (16 * kc + 8 * g >= d) continue;
-      float of[8], dof[8];
-      if (p.o_f32) load8<ATTN_F32, ATTN_CFG_BWD_O_NONTEMPORAL>(p.o, ro + 16 * kc, of);
-      else load8<IS_BF16 ? (int)ATTN_BF16 : (int)ATTN_F16, ATTN_CFG_BWD_O_NONTEMPORAL>(p.o, ro + 16 * kc, of);
-      unpack8<IS_BF16>(df[kc], dof);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) dd += dof[c] * of[c];
-    }
+    if (p.o_f32)
+      dd = row_dot_o<ATTN_F32, NKC, IS_BF16>(p.o, ro, df, g, d);
+    else
+      dd = row_dot_o<IS_BF16 ? (int)ATTN_BF16 : (int)ATTN_F16, NKC, IS_BF16>(p.o, ro, df, g, d);
     l2 = p.lse[(size_t)bh * Nq + my_q] * kLog2e;
   }
   dd += __shfl_xor(dd, 32);
