@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import subprocess
 import sys
 import time
@@ -49,8 +50,15 @@ KERNEL_SRC = os.path.join(ROOT, "io_aware_attention_flash_amd", "csrc", "attn_fw
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_digest():
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_digest(text=None):
+    """sha256[:16] of attn_fwd.hip's code: comments, trailing blanks and
+    empty lines removed, so an edit of the comments keeps recorded counters
+    valid and any edit of the code voids them."""
+    src = open(KERNEL_SRC).read() if text is None else text
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = "\n".join(line.rstrip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def measured_traffic(workload, out_dtype):

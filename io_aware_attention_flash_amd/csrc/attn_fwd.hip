@@ -12,8 +12,10 @@
 // back to the natural log ("Kernel 4", notes on exp2 and the saved L).
 //
 // gfx950 mapping (our design, not the page's):
-//  * each wave owns 32 query rows; a workgroup is 8 waves (256 rows) for
-//    d=128 and 4 waves (128 rows) for d=64.
+//  * each wave owns 32 query rows; a workgroup is 8 waves (256 rows, one
+//    per CU) or 4 waves (128 rows), and the K/V tile 32 to 128 keys: two
+//    tile shapes per head dimension are compiled, and the host picks one per
+//    problem (pick_launch16).
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_{bf16,f16}: with the 32x32 output
 //    layout each lane then holds the scores of ONE query row (lane & 31) for
 //    16 keys per 32-key block, so the row maximum is an in-lane max plus one
@@ -31,6 +33,10 @@
 //    of this one) with the softmax work spread across it: with operands read
 //    from LDS and vector work between the MFMAs, two waves per SIMD that
 //    each mix MFMAs with their own vector work keep the pipe busiest.
+//  * a second instance of each bf16/fp16 kernel reads and writes through the
+//    tensors' (batch, head, row) strides, with Nq query rows against Nk keys
+//    and head dims below 64 or 128 read as zero columns (attn_fwd_strided);
+//    the contiguous instance keeps those as compile-time constants.
 //  * fp32 inputs use a separate kernel on v_mfma_f32_32x32x2_f32.
 #include <hip/hip_runtime.h>
 

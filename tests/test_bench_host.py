@@ -53,3 +53,13 @@ def test_power_sampler_parses_and_skips_the_first_readings(monkeypatch):
     assert out["loaded_samples"] == 3
     assert out["socket_power_w_median"] == 1390.0
     assert out["gfx_clock_mhz_median"] == pytest.approx(1860.0)
+
+
+def test_digest_ignores_comments_only():
+    """The recorded counters stay valid across edits of comments and blank
+    lines, and any edit of the code voids them."""
+    code = "int f(int x) {\n  return x + 1;  // one more\n}\n"
+    same = "/* a note */\nint f(int x) {\n\n  return x + 1;   // another remark\n}\n"
+    other = "int f(int x) {\n  return x + 2;  // one more\n}\n"
+    assert bench.kernel_source_digest(code) == bench.kernel_source_digest(same)
+    assert bench.kernel_source_digest(code) != bench.kernel_source_digest(other)
