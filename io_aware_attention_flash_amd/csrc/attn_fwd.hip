@@ -247,7 +247,8 @@ using Tile16 = Shape16<D, D == 128 ? ATTN_CFG_FWD_WAVES_D128 : ATTN_CFG_FWD_WAVE
 #endif
 // Order of the two causal query tiles a workgroup takes: 0 runs the long one
 // first, 1 the short one (which then reads the keys the long one starts
-// with while they are fresh in L2).
+// with while they are fresh in L2), 2 alternates: pairs with an odd index run
+// the short tile first, the others the long one.
 #ifndef ATTN_CFG_CAUSAL_SHORT_FIRST
 #define ATTN_CFG_CAUSAL_SHORT_FIRST 0
 #endif
@@ -255,6 +256,11 @@ using Tile16 = Shape16<D, D == 128 ? ATTN_CFG_FWD_WAVES_D128 : ATTN_CFG_FWD_WAVE
 // read once) or plain (0).
 #ifndef ATTN_CFG_Q_NONTEMPORAL
 #define ATTN_CFG_Q_NONTEMPORAL 0
+#endif
+// Heads of one XCD when B*H is a multiple of 8: every eighth head (0: XCD x
+// runs heads x, x+8, ...) or a block of B*H/8 adjacent ones (1).
+#ifndef ATTN_CFG_HEAD_BLOCKED
+#define ATTN_CFG_HEAD_BLOCKED 0
 #endif
 // Causal workgroups take a pair of query tiles (long + short, 1) or one
 // tile each, longest first (0).
@@ -1158,7 +1164,7 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
     const int j = w >> 3;
     const int hl = j / per_head;
     t = j - hl * per_head;
-    bh = (hl << 3) | (w & 7);
+    bh = ATTN_CFG_HEAD_BLOCKED ? (w & 7) * (p.BH >> 3) + hl : (hl << 3) | (w & 7);
   } else {
     t = w / p.BH;
     bh = w - t * p.BH;
@@ -1173,8 +1179,10 @@ __global__ __launch_bounds__(S::THREADS, S::WG_PER_CU) void attn_fwd_16(FwdParam
   }
   const int q_long = p.nq - 1 - t, q_short = t;
   const int n_items = q_short < q_long ? 2 : 1;
-  const int qa = ATTN_CFG_CAUSAL_SHORT_FIRST && n_items == 2 ? q_short : q_long;
-  const int qb = ATTN_CFG_CAUSAL_SHORT_FIRST && n_items == 2 ? q_long : q_short;
+  const bool short_first = n_items == 2 && (ATTN_CFG_CAUSAL_SHORT_FIRST == 1 ||
+                                             (ATTN_CFG_CAUSAL_SHORT_FIRST == 2 && (t & 1)));
+  const int qa = short_first ? q_short : q_long;
+  const int qb = short_first ? q_long : q_short;
 #pragma unroll 1
   for (int k = 0; k < n_items; ++k) {
     // The second tile's copies reuse the LDS the first one's epilogue read.

@@ -50,12 +50,18 @@ KNOBS = {
                          what="forward tile at d=64: waves per workgroup x keys per K/V tile "
                               "(shipped: chosen per problem between 8x128 and 4x64 by a "
                               "round-count cost model)"),
-    "fwd_causal_short_first": dict(macro="ATTN_CFG_CAUSAL_SHORT_FIRST", values=[0, 1],
+    "fwd_causal_short_first": dict(macro="ATTN_CFG_CAUSAL_SHORT_FIRST", values=[0, 1, 2],
                                    pass_="fwd",
                                    workloads=["b2h32_n4096_d128_bf16_causal",
                                               "b1h16_n16384_d128_bf16_sigma3_causal"],
                                    what="causal workgroups run their short query tile first "
-                                        "(1) or their long one (0)"),
+                                        "(1), their long one (0), or alternate by pair (2)"),
+    "fwd_head_blocked": dict(macro="ATTN_CFG_HEAD_BLOCKED", values=[0, 1], pass_="fwd",
+                             workloads=["b2h32_n4096_d128_bf16_causal",
+                                        "b1h16_n16384_d128_bf16_sigma3_causal",
+                                        "b8h12_n3000_d64_f16", "b4h16_n1024_d64_bf16"],
+                             what="heads of one XCD: every eighth one (0) or a block of B*H/8 "
+                                  "adjacent ones (1)"),
     "fwd_causal_pairs": dict(macro="ATTN_CFG_CAUSAL_PAIRS", values=[1, 0], pass_="fwd",
                              workloads=["b2h32_n4096_d128_bf16_causal",
                                         "b1h16_n16384_d128_bf16_sigma3_causal"],
