@@ -1,5 +1,5 @@
 // General-layout attention forward for gfx950 (MI355X): the same operation
-// as attn_fwd, for the cases its tuned kernels do not take:
+// as attn_fwd (entry point attn_fwd_strided), for
 //  - a different number of keys than queries (cross-attention;
 //    "Programming an attention kernel in Triton", section "Kernel 4:
 //    bringing it together, a self-attention kernel", checks its kernel on
@@ -11,6 +11,10 @@
 //    dot product q.k, and the output columns past d are never written;
 //  - strided tensors: element (b, h, n, c) at b*sb + h*sh + n*sn + c (the
 //    Triton kernels of the same pages take per-dimension strides).
+// bf16/fp16 problems with row strides of at most 2^21 elements run on
+// attn_fwd's tuned kernels, whose strided instances cover all three cases
+// (fwd16_strided); the kernels below serve fp32 inputs and longer row
+// strides, and every problem when built with ATTN_CFG_STRIDED_TUNED=0.
 //
 // attn_gen_16 (bf16 / fp16): one workgroup per (head, 128 queries); 4 waves
 // of 32 queries each loop over 64-key tiles. Per 32-key block and wave:
