@@ -258,17 +258,17 @@ __device__ __forceinline__ void lds_barrier() {
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a source offset past any range
 
 // Tile of R rows x D 16-bit elements of a matrix with row stride sn, copied by
-// all 256 threads: instruction c fills 16-byte slots c*256 + tid; slot s holds
+// all THREADS threads: instruction c fills 16-byte slots c*THREADS + tid; slot s holds
 // physical chunk s % CPR of tile row s / CPR, i.e. logical chunk
 // (s % CPR) ^ swz(row). One instruction spans a whole number of swizzle
 // periods (16 rows), so the lane's source offset is that of c = 0 plus c rows
 // strides of RPI rows. A lane whose logical chunk starts at or past column d
 // reads from an offset beyond the range, which returns zeros: the columns
 // d .. D-1 of the tile are zero without any instruction in the loops.
-template <int D, int R>
+template <int D, int R, int THREADS = kThreads>
 struct TileCopy {
   static constexpr int CPR = D / 8;
-  static constexpr int RPI = kThreads / CPR;  // rows per instruction
+  static constexpr int RPI = THREADS / CPR;  // rows per instruction
   static constexpr int INS = R / RPI;
   static_assert(INS * RPI == R && RPI % 16 == 0, "tile copy shape");
   uint32_t off0;  // source byte offset of instruction 0, or kOutOfRange
@@ -287,7 +287,7 @@ struct TileCopy {
     const uint32_t ldsb = __builtin_amdgcn_readfirstlane(lds_addr(lds) + wave * 64 * 16);
 #pragma unroll
     for (int c = 0; c < INS; ++c)
-      dma16(rs, ldsb + c * kThreads * 16, off0 == kOutOfRange ? kOutOfRange : off0 + c * step);
+      dma16(rs, ldsb + c * THREADS * 16, off0 == kOutOfRange ? kOutOfRange : off0 + c * step);
   }
 };
 
@@ -395,19 +395,23 @@ __global__ __launch_bounds__(256) void bwd_prep(BwdParams p, int64_t rows) {
 // ---------------------------------------------------------------------------
 // bwd_dkdv
 // ---------------------------------------------------------------------------
-template <int D>
+// WAVES waves of 32 keys each: 4 (two workgroups per CU), or 8 at D = 128 in
+// a sweep build (one per CU).
+template <int D, int WAVES>
 struct DkdvShape {
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BLOCK_K = 32 * WAVES;        // keys per workgroup
   static constexpr int TILE = kTileQ * D;           // elements of a Q or dO tile
   static constexpr int STAGE = 2 * TILE + 512;      // Q, dO, LD (1 KB: one copy instruction)
-  static constexpr int V_ELEMS = kBlockK * D;
+  static constexpr int V_ELEMS = BLOCK_K * D;
   static constexpr int LDS_ELEMS = V_ELEMS + 2 * STAGE;
 };
 
-template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
-  using S = DkdvShape<D>;
-  using QCopy = TileCopy<D, kTileQ>;
-  using VCopy = TileCopy<D, kBlockK>;
+template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void bwd_dkdv(BwdParams p) {
+  using S = DkdvShape<D, WAVES>;
+  using QCopy = TileCopy<D, kTileQ, S::THREADS>;
+  using VCopy = TileCopy<D, S::BLOCK_K, S::THREADS>;
   constexpr int NKC = D / 16, NCB = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t lds[S::LDS_ELEMS];
 
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
   const int kbk = blockIdx.x / p.BH;  // small k0 first: causal blocks with most work start first
   const int bh = blockIdx.x - kbk * p.BH;
   const int Nq = p.Nq, Nk = p.Nk;
-  const int k0 = kbk * kBlockK, kw0 = k0 + 32 * wave;
+  const int k0 = kbk * S::BLOCK_K, kw0 = k0 + 32 * wave;
   const int d = p.d;
   const uint16_t *Qh = reinterpret_cast<const uint16_t *>(p.q) + head_off(p.qs, bh, p.H);
   const uint16_t *Kh = reinterpret_cast<const uint16_t *>(p.k) + head_off(p.ks, bh, p.H);
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv(BwdParams p) {
     }
   };
 
-  // V block (this workgroup's 128 keys) into LDS, and the first query tile.
+  // V block (this workgroup's keys) into LDS, and the first query tile.
   {
     VCopy vc;
     vc.init(tid, p.vs[2], d);
@@ -936,19 +940,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_f32(BwdParams p) {
 typedef void (*KernelFn)(BwdParams);
 typedef void (*PrepFn)(BwdParams, int64_t);
 
+// Waves per dK/dV workgroup for 16-bit inputs. 8 (at D = 128 only: one
+// workgroup per CU, each Q and dO tile in LDS serving 256 keys) measured
+// 0.4-5.5% slower than 4 at every d = 128 workload timed, so 4 ships and the
+// 8-wave kernels are built only for a sweep (-DATTN_CFG_BWD_DKDV_WAVES=8).
+#ifndef ATTN_CFG_BWD_DKDV_WAVES
+#define ATTN_CFG_BWD_DKDV_WAVES 4
+#endif
+static_assert(ATTN_CFG_BWD_DKDV_WAVES == 4 || ATTN_CFG_BWD_DKDV_WAVES == 8, "dK/dV waves");
+
 template <int D, bool IS_BF16, bool CAUSAL, bool GRAD_F32>
-void pick3(KernelFn &dkdv, KernelFn &dq) {
-  dkdv = bwd_dkdv<D, IS_BF16, CAUSAL, GRAD_F32>;
+void pick3(int waves, KernelFn &dkdv, KernelFn &dq) {
+  dkdv = bwd_dkdv<D, IS_BF16, CAUSAL, GRAD_F32, 4>;
+  if constexpr (D == 128 && ATTN_CFG_BWD_DKDV_WAVES == 8)
+    if (waves == 8) dkdv = bwd_dkdv<D, IS_BF16, CAUSAL, GRAD_F32, 8>;
   dq = bwd_dq<D, IS_BF16, CAUSAL, GRAD_F32>;
 }
 
 template <int D, bool IS_BF16>
-void pick2(bool causal, bool grad_f32, KernelFn &dkdv, KernelFn &dq) {
+void pick2(bool causal, bool grad_f32, int waves, KernelFn &dkdv, KernelFn &dq) {
   if (causal) {
-    if (grad_f32) pick3<D, IS_BF16, true, true>(dkdv, dq); else pick3<D, IS_BF16, true, false>(dkdv, dq);
+    if (grad_f32) pick3<D, IS_BF16, true, true>(waves, dkdv, dq);
+    else pick3<D, IS_BF16, true, false>(waves, dkdv, dq);
   } else {
-    if (grad_f32) pick3<D, IS_BF16, false, true>(dkdv, dq); else pick3<D, IS_BF16, false, false>(dkdv, dq);
+    if (grad_f32) pick3<D, IS_BF16, false, true>(waves, dkdv, dq);
+    else pick3<D, IS_BF16, false, false>(waves, dkdv, dq);
   }
+}
+
+// The 8-wave build takes D = 128 problems whose V block of 256 rows spans
+// less than 2^31 bytes.
+int dkdv_waves(int64_t D, int64_t v_row_bytes) {
+  return ATTN_CFG_BWD_DKDV_WAVES == 8 && D == 128 && v_row_bytes * 256 < (int64_t(1) << 31) ? 8 : 4;
 }
 
 template <int D>
@@ -1052,7 +1075,9 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
                     int causal, float scale, attn_dtype in_dtype, attn_dtype o_dtype,
                     attn_dtype grad_dtype, void *ld, void *stream) {
   const int64_t D = d <= 64 ? 64 : 128;  // the kernels' head dim; columns past d are zeros
-  const int64_t nkb = (Nk + kBlockK - 1) / kBlockK, nqb = (Nq + kBlockQ - 1) / kBlockQ;
+  const int waves = in_dtype == ATTN_F32 ? 4 : dkdv_waves(D, w.vs[2] * elem_bytes(in_dtype));
+  const int64_t block_k = 32 * waves;  // keys per dK/dV workgroup
+  const int64_t nkb = (Nk + block_k - 1) / block_k, nqb = (Nq + kBlockQ - 1) / kBlockQ;
   const int64_t rows = B * H * Nq;
   const int64_t lpr = D / 8;
   const int64_t prep_blocks = (rows * lpr + 255) / 256;
@@ -1088,11 +1113,11 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
   if (in_dtype == ATTN_F32) {
     if (D == 64) pick_f32<64>(causal != 0, fdkdv, fdq); else pick_f32<128>(causal != 0, fdkdv, fdq);
   } else if (D == 64) {
-    if (in_dtype == ATTN_BF16) pick2<64, true>(causal != 0, grad_f32, fdkdv, fdq);
-    else pick2<64, false>(causal != 0, grad_f32, fdkdv, fdq);
+    if (in_dtype == ATTN_BF16) pick2<64, true>(causal != 0, grad_f32, waves, fdkdv, fdq);
+    else pick2<64, false>(causal != 0, grad_f32, waves, fdkdv, fdq);
   } else {
-    if (in_dtype == ATTN_BF16) pick2<128, true>(causal != 0, grad_f32, fdkdv, fdq);
-    else pick2<128, false>(causal != 0, grad_f32, fdkdv, fdq);
+    if (in_dtype == ATTN_BF16) pick2<128, true>(causal != 0, grad_f32, waves, fdkdv, fdq);
+    else pick2<128, false>(causal != 0, grad_f32, waves, fdkdv, fdq);
   }
   hipStream_t st = (hipStream_t)stream;
   void *args[] = {&p};
@@ -1116,7 +1141,7 @@ attn_status bwd_run(const void *q, const void *k, const void *v, const void *o,
                           dim3(kThreads), args, 0, st);
     if (err == hipSuccess)
       err = hipLaunchKernel(reinterpret_cast<const void *>(fdkdv), dim3((unsigned)(nkb * B * H)),
-                            dim3(kThreads), args, 0, st);
+                            dim3((unsigned)(64 * waves)), args, 0, st);
   }
   if (err != hipSuccess) {
     attn_internal::set_last_hip_error((int)err);

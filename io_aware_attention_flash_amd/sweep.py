@@ -111,6 +111,12 @@ KNOBS = {
                           workloads=["b2h32_n4096_d128_bf16_causal",
                                      "b8h12_n3000_d64_f16"],
                           what="keys per step of the backward's dQ kernel"),
+    "bwd_dkdv_waves": dict(macro="ATTN_CFG_BWD_DKDV_WAVES", values=[4, 8],
+                           pass_="bwd",
+                           workloads=["b2h32_n4096_d128_bf16_causal",
+                                      "b1h16_n16384_d128_bf16_sigma3_causal",
+                                      "b4h16_n1024_d128_bf16", "b8h12_n3000_d128_bf16"],
+                           what="waves per dK/dV workgroup at d=128 (32 keys each)"),
     "bwd_lookahead": dict(macro="ATTN_CFG_BWD_LOOKAHEAD", values=[2, 1], pass_="bwd",
                           workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
                           what="MFMA steps by which the backward's LDS operand reads run ahead "
