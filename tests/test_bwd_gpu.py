@@ -444,3 +444,41 @@ def test_bwd_full_size_sampled(name):
         terms = [t[0, 0][rows] for t in terms]
         extra = [e[0, 0][rows] for e in extra]
         check_grads(got, (rq, rk, rv), terms, extra, u, "%s head %d" % (name, bh))
+
+
+# ---------------------------------------------------- offsets past 2^31
+
+def test_bwd_offsets_past_2_31():
+    """B2^12 H2^8 N64 d64 bf16 causal: 2^32 elements per tensor, so element
+    offsets pass 2^31 (byte offsets 2^32) in every input and gradient, with
+    2^20 workgroups per launch. GPU forward then backward; whole heads on both
+    sides of the crossing, and the first and last head, against the oracle.
+    Inputs come from torch's seeded generator on the GPU; only the compared
+    heads are copied back."""
+    B, H, N, d, dt, causal = 4096, 256, 64, 64, "bf16", True
+    _say("backward, offsets past 2^31")
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(32)
+    q, k, v, dout = (torch.randn((B, H, N, d), generator=gen, device=dev, dtype=DT[dt])
+                     for _ in range(4))
+    scale = _scale(d)
+    o, lse = binding.attn_fwd(q, k, v, causal=causal, scale=scale, out_dtype=torch.float32)
+    dq, dk, dv = binding.attn_bwd(q, k, v, o, lse, dout, causal=causal, scale=scale,
+                                  grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for x in (dq, dk, dv):
+        assert bool(torch.isfinite(x).all())
+    cross = (1 << 31) // (N * d)
+    for bh in (0, cross - 1, cross, B * H - 1):
+        b, h = divmod(bh, H)
+        qh, kh, vh, dh = (x[b:b + 1, h:h + 1].cpu() for x in (q, k, v, dout))
+        ref = oracle.attn_bwd_oracle(qh, kh, vh, dh, causal=causal, scale=scale)
+        ro, rl = oracle.attn_oracle(qh, kh, vh, causal=causal, scale=scale)
+        dD = (dh.double() * (o[b:b + 1, h:h + 1].cpu().double() - torch.from_numpy(ro))).sum(-1)
+        dL = lse[b:b + 1, h:h + 1].cpu().double() - torch.from_numpy(rl)
+        terms, extra = _terms(qh, kh, vh, dh, causal, scale, dD=dD, dL=dL)
+        got = [x[b:b + 1, h:h + 1].cpu() for x in (dq, dk, dv)]
+        check_grads(got, ref, terms, extra, U[dt], "head %d of %d" % (bh, B * H))
+    del q, k, v, dout, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()

@@ -220,6 +220,49 @@ def test_long_sequence_sampled(case):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+# ---------------------------------------------------- offsets past 2^31
+BIG_CASES = [
+    # (B, H, N, d, dtype, causal, layout): 2^32 elements per tensor, so the
+    # element offsets of the later heads pass 2^31 (byte offsets 2^32) and the
+    # grid has 2^20 workgroups; "bnhd" passes [B, N, H, d] tensors as
+    # transposed views
+    (4096, 256, 64, 64, "bf16", True, "bhnd"),
+    (2048, 512, 32, 128, "f16", False, "bhnd"),
+    (4096, 256, 64, 64, "bf16", False, "bnhd"),
+]
+
+
+@pytest.mark.parametrize("case", BIG_CASES, ids=lambda c: "B%dH%dN%d_d%d_%s_%s_%s" % (
+    c[0], c[1], c[2], c[3], c[4], "causal" if c[5] else "full", c[6]))
+def test_offsets_past_2_31(case):
+    """Whole heads on both sides of element offset 2^31, the first and the
+    last head against the oracle. Inputs come from torch's seeded generator
+    on the GPU (2^32 values per tensor); only the compared heads are copied
+    back for the oracle."""
+    B, H, N, d, dt, causal, layout = case
+    _say("offsets past 2^31", case)
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(31)
+    shape = (B, H, N, d) if layout == "bhnd" else (B, N, H, d)
+    q, k, v = (torch.randn(shape, generator=gen, device=dev, dtype=DT[dt]) for _ in range(3))
+    if layout == "bnhd":
+        q, k, v = (x.transpose(1, 2) for x in (q, k, v))
+    sc = _scale(d)
+    o, lse = binding.attn_fwd(q, k, v, causal=causal, scale=sc, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    cross = (1 << 31) // (N * d)  # first head whose elements start at offset 2^31
+    for bh in (0, cross - 1, cross, B * H - 1):
+        b, h = divmod(bh, H)
+        qh, kh, vh = (x[b:b + 1, h:h + 1].cpu() for x in (q, k, v))
+        ref_o, ref_l = oracle.attn_oracle(qh, kh, vh, causal=causal, scale=sc)
+        check_close(o[b:b + 1, h:h + 1].cpu().numpy(), lse[b:b + 1, h:h + 1].cpu().numpy(),
+                    ref_o, ref_l, "head %d of %d" % (bh, B * H))
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------- special cases
 def test_exercise5_embedded():
     """Exercise 5 of the Triton chapter inside a d=64 head: q0 = e0,
