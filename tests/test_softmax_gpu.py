@@ -98,3 +98,24 @@ def test_large_logits_and_inf():
     assert y[0, 7].item() == 1.0 and torch.count_nonzero(y[0]) == 1
     assert y[1, 5].item() == 1.0
     assert torch.all(y[2, 100:] == 0) and abs(y[2, :100].sum().item() - 1.0) <= 1e-6
+
+
+@pytest.mark.parametrize("M,N,dt", [(1 << 19, 8192, "bf16"), (1 << 18, 16384, "f32")],
+                         ids=["M524288N8192_bf16", "M262144N16384_f32"])
+def test_offsets_past_2_31(M, N, dt):
+    """2^32 elements in one matrix: the element offsets of the later rows pass
+    2^31 (byte offsets 2^32). Rows on both sides of the crossing and the last
+    row against the oracle; inputs come from torch's seeded generator on the
+    GPU and only the compared rows are copied back. (Offsets within a row stay
+    below N <= 2^30; the row base is 64-bit.)"""
+    print("offsets past 2^31", (M, N, dt), flush=True)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(43)
+    x = torch.randn((M, N), generator=gen, device=DEV, dtype=DT[dt])
+    y = binding.row_softmax(x, out_dtype=DT[dt])
+    torch.cuda.synchronize()
+    cross = (1 << 31) // N
+    for r in sorted({0, max(cross - 1, 0), min(cross, M - 1), M - 1}):
+        _check(y[r:r + 1], x[r:r + 1].cpu(), dt, "row %d of %d" % (r, M))
+    del x, y
+    torch.cuda.empty_cache()
