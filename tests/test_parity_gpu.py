@@ -229,6 +229,8 @@ BIG_CASES = [
     (4096, 256, 64, 64, "bf16", True, "bhnd"),
     (2048, 512, 32, 128, "f16", False, "bhnd"),
     (4096, 256, 64, 64, "bf16", False, "bnhd"),
+    (4096, 256, 64, 64, "f32", True, "bhnd"),    # the fp32 kernel
+    (4096, 256, 64, 64, "f32", False, "bnhd"),   # the general kernel (fp32 views)
 ]
 
 
