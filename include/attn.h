@@ -227,8 +227,12 @@ attn_status attn_bwd_qk(const void *q, const void *k, const void *v, const void 
  * workspace is attn_bwd_qk's. Each view must have non-negative strides, a
  * row stride >= d, rows starting 16-byte aligned (base and every stride a
  * multiple of 16 bytes), every offset below 2^47 elements, and 128 rows
- * spanning less than 2^31 bytes; otherwise ATTN_ERR_UNSUPPORTED. Every
- * other argument, check, error and result is that of attn_bwd_qk.
+ * spanning less than 2^31 bytes; otherwise ATTN_ERR_UNSUPPORTED. The
+ * inputs may share memory (a stride of 0 over heads lets H query heads read
+ * one K/V head: multi- or grouped-query attention); the rows of dq, dk and
+ * dv must not (ATTN_ERR_UNSUPPORTED otherwise): dK and dV are written per
+ * query head, and a caller sharing K/V heads sums them over each group.
+ * Every other argument, check, error and result is that of attn_bwd_qk.
  */
 attn_status attn_bwd_strided(const void *q, const int64_t *q_strides, const void *k,
                              const int64_t *k_strides, const void *v, const int64_t *v_strides,
@@ -281,6 +285,11 @@ attn_status attn_bwd_noalloc(const void *q, const void *k, const void *v, const 
  *              bytes, strides non-negative, the row stride >= d, and every
  *              offset below 2^47 elements; for bf16/fp16, 64 rows of K or V
  *              must span less than 2^31 bytes. Otherwise ATTN_ERR_UNSUPPORTED.
+ *              q, k and v may share memory: a head stride of 0 lets every
+ *              query head read one K/V head (multi-query attention), and q
+ *              seen as [B*Hkv][G][Nq][d] with k, v as [B*Hkv][G][Nk][d] of
+ *              head stride 0 gives grouped-query attention. The rows of o
+ *              must not overlap (ATTN_ERR_UNSUPPORTED otherwise).
  * lse        : device, [B][H][Nq] contiguous fp32; written.
  * causal     : requires Nq == Nk (else ATTN_ERR_SHAPE).
  * d          : a multiple of 8 in [8, 128] (else ATTN_ERR_UNSUPPORTED).

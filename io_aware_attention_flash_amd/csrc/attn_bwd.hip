@@ -1029,6 +1029,28 @@ bool view_ok(const void *ptr, const int64_t s[3], int64_t B, int64_t H, int64_t 
   return s[2] * eb * 128 < (int64_t(1) << 31);
 }
 
+// Whether the B*H blocks of n rows x d elements of a view with (batch, head,
+// row) strides s cover disjoint elements, so that no two output rows share
+// memory (an expanded view, stride 0 over heads or batches, is refused).
+// Ordered by stride, each dimension of extent > 1 must step past everything
+// inside it; the row stride is already >= d.
+bool out_view_disjoint(const int64_t s[3], int64_t B, int64_t H, int64_t n, int64_t d) {
+  int64_t st[3] = {s[0], s[1], s[2]}, ext[3] = {B, H, n};
+  for (int i = 0; i < 3; ++i)  // ascending stride
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i] || (st[j] == st[i] && ext[j] > ext[i])) {
+        const int64_t a = st[i], b = ext[i];
+        st[i] = st[j], ext[i] = ext[j], st[j] = a, ext[j] = b;
+      }
+  int64_t span = d;  // elements covered by the dimensions inside the current one
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] == 1) continue;
+    if (st[i] < span) return false;
+    span += (ext[i] - 1) * st[i];
+  }
+  return true;
+}
+
 // Argument checks shared by the backward's entry points; no HIP call.
 attn_status bwd_check(const void *q, const void *k, const void *v, const void *o,
                       const float *lse, const void *dout, void *dq, void *dk, void *dv,
@@ -1062,7 +1084,9 @@ attn_status views_check(const void *q, const void *k, const void *v, const void 
   if (!view_ok(q, w.qs, B, H, Nq, d, ei) || !view_ok(k, w.ks, B, H, Nk, d, ei) ||
       !view_ok(v, w.vs, B, H, Nk, d, ei) || !view_ok(o, w.os, B, H, Nq, d, eo) ||
       !view_ok(dout, w.dos, B, H, Nq, d, ei) || !view_ok(dq, w.dqs, B, H, Nq, d, eg) ||
-      !view_ok(dk, w.dks, B, H, Nk, d, eg) || !view_ok(dv, w.dvs, B, H, Nk, d, eg))
+      !view_ok(dk, w.dks, B, H, Nk, d, eg) || !view_ok(dv, w.dvs, B, H, Nk, d, eg) ||
+      !out_view_disjoint(w.dqs, B, H, Nq, d) || !out_view_disjoint(w.dks, B, H, Nk, d) ||
+      !out_view_disjoint(w.dvs, B, H, Nk, d))
     return ATTN_ERR_UNSUPPORTED;
   return ATTN_OK;
 }

@@ -677,6 +677,28 @@ bool view_ok(const void *ptr, const int64_t s[3], int64_t B, int64_t H, int64_t 
   return true;
 }
 
+// Whether the B*H blocks of n rows x d elements of a view with (batch, head,
+// row) strides s cover disjoint elements, so that no two output rows share
+// memory (an expanded view, stride 0 over heads or batches, is refused).
+// Ordered by stride, each dimension of extent > 1 must step past everything
+// inside it; the row stride is already >= d.
+bool out_view_disjoint(const int64_t s[3], int64_t B, int64_t H, int64_t n, int64_t d) {
+  int64_t st[3] = {s[0], s[1], s[2]}, ext[3] = {B, H, n};
+  for (int i = 0; i < 3; ++i)  // ascending stride
+    for (int j = i + 1; j < 3; ++j)
+      if (st[j] < st[i] || (st[j] == st[i] && ext[j] > ext[i])) {
+        const int64_t a = st[i], b = ext[i];
+        st[i] = st[j], ext[i] = ext[j], st[j] = a, ext[j] = b;
+      }
+  int64_t span = d;  // elements covered by the dimensions inside the current one
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] == 1) continue;
+    if (st[i] < span) return false;
+    span += (ext[i] - 1) * st[i];
+  }
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -706,7 +728,8 @@ attn_status attn_fwd_strided(const void *q, const int64_t *q_strides, const void
   fill_strides(p.os, o_strides, H, Nq, d);
   const int eb = elem_bytes(in_dtype), ob = elem_bytes(out_dtype);
   if (!view_ok(q, p.qs, B, H, Nq, d, eb) || !view_ok(k, p.ks, B, H, Nk, d, eb) ||
-      !view_ok(v, p.vs, B, H, Nk, d, eb) || !view_ok(o, p.os, B, H, Nq, d, ob))
+      !view_ok(v, p.vs, B, H, Nk, d, eb) || !view_ok(o, p.os, B, H, Nq, d, ob) ||
+      !out_view_disjoint(p.os, B, H, Nq, d))
     return ATTN_ERR_UNSUPPORTED;
   // a key tile (up to kTileKMax rows) of K or V must fit the 32-bit range of a buffer descriptor
   if (in_dtype != ATTN_F32 && (p.ks[2] * eb * kTileKMax >= (int64_t(1) << 31) ||

@@ -185,6 +185,9 @@ def test_bwd_error_paths_need_no_gpu(lib, args, code):
     (dict(q_st=(-4096, 4096, 64)), 3),                    # negative stride
     (dict(k_st=(1 << 20, 1 << 14, 32)), 3),               # row stride < d
     (dict(v_st=(1 << 20, 1 << 14, 68)), 3),               # row not 16-byte aligned (bf16)
+    (dict(o_st=(4096, 0, 64)), 3),                        # output heads alias (stride 0)
+    (dict(o_st=(4096, 32, 64)), 3),                       # output heads overlap (stride < d)
+    (dict(o_st=(4096, 64, 64)), 3),                       # head and row strides equal
     (dict(scale=float("nan")), 4),
 ])
 def test_strided_error_paths_need_no_gpu(lib, args, code):
@@ -258,6 +261,8 @@ def test_bwd_noalloc_error_paths_need_no_gpu(lib, args, code):
     (dict(dq_st=(1 << 20, 1 << 14, 66)), 3),              # gradient row not aligned (fp32)
     (dict(o_st=(1 << 47, 1 << 14, 64)), 3),               # offsets beyond 2^47 elements
     (dict(do_st=(1 << 30, 1 << 24, 1 << 23)), 3),         # 128 rows span >= 2^31 bytes
+    (dict(dq_st=(1 << 20, 0, 64)), 3),                    # gradient heads alias (stride 0)
+    (dict(dq_st=(0, 1 << 14, 64)), 3),                    # gradient batches alias (B = 2)
     (dict(scale=float("nan")), 4),
     (dict(ws=0), 6),
 ])

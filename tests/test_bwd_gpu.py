@@ -482,3 +482,46 @@ def test_bwd_offsets_past_2_31():
         check_grads(got, ref, terms, extra, U[dt], "head %d of %d" % (bh, B * H))
     del q, k, v, dout, o, lse, dq, dk, dv
     torch.cuda.empty_cache()
+
+
+def test_bwd_shared_kv_heads():
+    """Grouped-query attention through stride-0 views: Q as [B*Hkv, G, N, d],
+    K and V as [B*Hkv, G, N, d] views of [B, Hkv, N, d] tensors with head
+    stride 0. The backward reads the shared K and V in place and writes dK
+    and dV per query head (disjoint outputs), which must equal the oracle's
+    gradients for materialised copies of K and V; through autograd, the
+    expand's own backward then sums them over each group."""
+    B, H, Hkv, N, d, dt, causal = 2, 8, 2, 193, 128, "bf16", True
+    G = H // Hkv
+    q = make_qkv(B, H, N, d, dt, 1.0, seed=37)[0]
+    _, kk, vv = make_qkv(B, Hkv, N, d, dt, 1.0, seed=38)
+    dout = make_dout(B, H, N, d, dt, seed=37)
+    scale = _scale(d)
+    dev = torch.device("cuda:0")
+    q4, do4 = (x.to(dev).view(B * Hkv, G, N, d) for x in (q, dout))
+    k4, v4 = (x.to(dev).reshape(B * Hkv, 1, N, d).expand(B * Hkv, G, N, d) for x in (kk, vv))
+    o, lse = binding.attn_fwd(q4, k4, v4, causal=causal, scale=scale, out_dtype=torch.float32)
+    dq, dk, dv = binding.attn_bwd(q4, k4, v4, o, lse, do4, causal=causal, scale=scale,
+                                  grad_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kr, vr = (x.repeat_interleave(G, dim=1) for x in (kk, vv))
+    ref = oracle.attn_bwd_oracle(q, kr, vr, dout, causal=causal, scale=scale)
+    ro, rl = oracle.attn_oracle(q, kr, vr, causal=causal, scale=scale)
+    dD = (dout.double() * (o.view(B, H, N, d).cpu().double() - torch.from_numpy(ro))).sum(-1)
+    dL = lse.view(B, H, N).cpu().double() - torch.from_numpy(rl)
+    terms, extra = _terms(q, kr, vr, dout, causal, scale, dD=dD, dL=dL)
+    got = [x.view(B, H, N, d).cpu() for x in (dq, dk, dv)]
+    check_grads(got, ref, terms, extra, U[dt], "shared K/V heads")
+    # autograd over the stride-0 views: the group sums land in the shared tensors
+    from io_aware_attention_flash_amd.ops import flash_attn_func
+    kg, vg = (x.to(dev).reshape(B * Hkv, 1, N, d).clone().requires_grad_() for x in (kk, vv))
+    qg = q4.clone().requires_grad_()
+    flash_attn_func(qg, kg.expand(B * Hkv, G, N, d), vg.expand(B * Hkv, G, N, d),
+                    causal=causal, scale=scale).backward(do4)
+    torch.cuda.synchronize()
+    for name, g, per_head in (("dK", kg.grad, dk), ("dV", vg.grad, dv)):
+        want = per_head.double().sum(1, keepdim=True)
+        rel = float((g.double() - want).norm() / want.norm())
+        print("shared K/V heads, autograd %s: relative error %.2e" % (name, rel), flush=True)
+        # bf16 gradients per head, summed: a few units of bf16 rounding
+        assert torch.isfinite(g).all() and rel <= 4 * U[dt], name

@@ -276,3 +276,39 @@ def test_input_dtype_output():
     ro, _ = oracle.attn_oracle(q, k, v, causal=False, scale=scale)
     err = np.abs(o.cpu().double().numpy() - ro)
     assert np.all(err <= 1e-2 + 0.5 * np.abs(ro) * 2.0 ** -8 + 1e-30)
+
+
+# Shared key/value heads through stride-0 views: multi-query attention (one
+# K/V head for all H query heads) and grouped-query attention (Hkv K/V heads,
+# each shared by G = H / Hkv query heads, by viewing Q as [B*Hkv, G, N, d] and
+# K, V as [B*Hkv, G, N, d] with head stride 0). The kernels only read K and V,
+# so aliased inputs need no copy; the oracle gets materialised copies.
+SHARED_KV = [
+    # (B, H, Hkv, Nq, Nk, d, dtype, causal)
+    (2, 8, 1, 300, 300, 128, "bf16", True),
+    (2, 8, 2, 257, 257, 64, "f16", False),
+    (1, 12, 4, 200, 517, 128, "bf16", False),
+    (2, 6, 3, 190, 190, 96, "bf16", True),
+    (1, 4, 1, 100, 100, 64, "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", SHARED_KV, ids=lambda c: "B%dH%dHkv%dNq%dNk%dd%d_%s_%s" % (
+    c[:7] + ("causal" if c[7] else "full",)))
+def test_shared_kv_heads(case):
+    B, H, Hkv, Nq, Nk, d, dt, causal = case
+    G = H // Hkv
+    print("case shared K/V heads", case, flush=True)
+    q = make_qkv(B, H, Nq, d, dt, 1.0, seed=35)[0]
+    _, kk, vv = make_qkv(B, Hkv, Nk, d, dt, 1.0, seed=36)
+    scale = _scale(d)
+    qd, kd, vd = q.to(DEV), kk.to(DEV), vv.to(DEV)
+    # [B*Hkv, G, n, d] views; K and V repeat each of their heads G times (stride 0)
+    q4 = qd.view(B * Hkv, G, Nq, d)
+    k4, v4 = (x.reshape(B * Hkv, 1, Nk, d).expand(B * Hkv, G, Nk, d) for x in (kd, vd))
+    assert k4.stride(1) == 0 and v4.stride(1) == 0
+    o, lse = binding.attn_fwd(q4, k4, v4, causal=causal, scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kr, vr = (x.repeat_interleave(G, dim=1) for x in (kk, vv))  # [B, H, Nk, d] copies
+    _check(o.view(B, H, Nq, d), lse.view(B, H, Nq), q, kr, vr, causal, scale,
+           "shared K/V %s" % (case,))
