@@ -114,7 +114,7 @@ attn_status attn_fwd(const void *q, const void *k, const void *v, void *o, float
  * For bf16 inputs with N >= 8192 the bf16 -> fp16 conversion of V (see
  * in_dtype above) runs once per element in a first pass that writes an
  * fp16 copy of V, B*H*N*d*2 bytes, into the workspace, instead of once per
- * 128-row query tile inside the attention kernel. Every other problem, and
+ * query tile inside the attention kernel. Every other problem, and
  * any invalid argument set, gives 0. No HIP call is made.
  */
 size_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, attn_dtype in_dtype);
