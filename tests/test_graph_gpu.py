@@ -1,4 +1,5 @@
-"""The entry points captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+"""The entry points captured in a HIP graph (torch.cuda.CUDAGraph) and replayed,
+and run on two streams at once.
 
 The C entry points only enqueue kernels on the caller's stream (no
 allocation, no memset, no synchronisation), so a caller may capture them in
@@ -179,3 +180,41 @@ def test_backward_graph(noalloc):
         return gs
 
     _replays(g, refill, grads, eager, "backward (noalloc=%s)" % noalloc)
+
+
+def test_two_streams_at_once():
+    """The library keeps no per-call state: a forward and backward on one
+    stream and a forward on another, enqueued alternately so that they can
+    overlap on the GPU, give the same bits as the same calls made one after
+    another on the current stream."""
+    dev = torch.device("cuda:0")
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    qa, ka, va = (x.to(dev) for x in make_qkv(2, 4, 1000, 128, "bf16", 1.0, seed=71))
+    da = make_dout(2, 4, 1000, 128, "bf16", seed=71).to(dev)
+    qb, kb, vb = (x.to(dev) for x in make_qkv(2, 3, 777, 64, "f16", 1.0, seed=72))
+    sca, scb = _scale(128), _scale(64)
+
+    def run_a():
+        o, lse = binding.attn_fwd(qa, ka, va, causal=True, scale=sca, out_dtype=torch.float32)
+        g = binding.attn_bwd(qa, ka, va, o, lse, da, causal=True, scale=sca,
+                             grad_dtype=torch.float32)
+        return [o, lse, *g]
+
+    def run_b():
+        return list(binding.attn_fwd(qb, kb, vb, causal=False, scale=scb,
+                                     out_dtype=torch.float32))
+
+    want_a, want_b = run_a(), run_b()
+    torch.cuda.synchronize()
+    got = []
+    for _ in range(3):
+        with torch.cuda.stream(sa):
+            ga = run_a()
+        with torch.cuda.stream(sb):
+            gb = run_b()
+        got.append((ga, gb))
+    torch.cuda.synchronize()
+    for r, (ga, gb) in enumerate(got):
+        for i, (x, y) in enumerate(zip(ga + gb, want_a + want_b)):
+            assert torch.equal(x, y), "round %d output %d differs" % (r, i)
+    print("two streams: 3 rounds equal the sequential calls", flush=True)
