@@ -4,12 +4,13 @@
 // Softmax": each row is read from HBM once and written once, with the
 // maximum, the exponentials and the sum formed on chip.
 //
-// The kernel is bound by HBM. A row of up to 4096 columns belongs to one
-// wave (four rows per workgroup) and lives in its registers, so the
-// reductions are wave-wide (no LDS); a row of up to 16384 or 65536 columns
-// belongs to a workgroup of 4 or 16 waves and the reductions add one LDS
-// exchange; longer rows take two passes (an online maximum and sum, then the
-// normalised write: two reads and one write). Loads are 16-byte
+// The kernel is bound by HBM. A short row belongs to one wave (four rows per
+// workgroup) and lives in its registers, so the reductions are wave-wide (no
+// LDS): up to 2048 columns of 16-bit input, 1024 of fp32. Longer rows belong
+// to a workgroup of 4 waves (up to 8192 16-bit or 4096 fp32 columns) or 16
+// (up to 65536) and the reductions add one LDS exchange; longer rows still
+// take two passes (an online maximum and sum, then the normalised write: two
+// reads and one write). Loads are 16-byte
 // vectors when the row pointers, the strides and N allow it, and coalesced
 // element loads otherwise. Arithmetic is fp32; the exponential is
 // v_exp_f32 on x * log2(e) - max * log2(e).
@@ -88,6 +89,24 @@ constexpr int rows_threads() { return WPR == 1 ? 256 : 64 * WPR; }
 #ifndef ATTN_CFG_SM_NONTEMPORAL
 #define ATTN_CFG_SM_NONTEMPORAL 1
 #endif
+// Values per lane that a one- or four-wave row holds in registers, for
+// fp32 and for 16-bit inputs (at most 64). Fewer values per lane send rows
+// to more waves sooner, which keeps more waves per CU loading: with 16,
+// fp32 rows of 1025 to 4096 columns take four waves; with 32, 16-bit rows
+// of 2049 to 4096 columns do. Measured against 64 (interleaved, M x N of
+// 2^27 elements): fp32 +7.0% to +7.6% at 2048 and 4096 columns, +2.2% to
+// +5.2% at 8192 and 16384; bf16 +4.7% at 4096, +1.5% at 16384, equal at 512
+// and 2048. 16 for 16-bit rows lost 10-18% at 2048 and 8192 columns.
+#ifndef ATTN_CFG_SM_F32_VPL_MAX
+#define ATTN_CFG_SM_F32_VPL_MAX 16
+#endif
+#ifndef ATTN_CFG_SM_H_VPL_MAX
+#define ATTN_CFG_SM_H_VPL_MAX 32
+#endif
+static_assert(ATTN_CFG_SM_F32_VPL_MAX == 16 || ATTN_CFG_SM_F32_VPL_MAX == 32 ||
+                  ATTN_CFG_SM_F32_VPL_MAX == 64, "fp32 values per lane");
+static_assert(ATTN_CFG_SM_H_VPL_MAX == 16 || ATTN_CFG_SM_H_VPL_MAX == 32 ||
+                  ATTN_CFG_SM_H_VPL_MAX == 64, "16-bit values per lane");
 template <typename V>
 __device__ __forceinline__ V load_once(const V *p) {
   if (ATTN_CFG_SM_NONTEMPORAL) return __builtin_nontemporal_load(p);
@@ -292,9 +311,10 @@ attn_status attn_row_softmax(const void *x, int64_t x_row_stride, void *y, int64
                    (y_row_stride * eo) % 16 == 0 && N % ch == 0;
   int wpr = 1, vpl = 8;
   bool longrow = false;
-  if (N <= 64 * 64) {
+  const int64_t v14 = ei == 4 ? ATTN_CFG_SM_F32_VPL_MAX : ATTN_CFG_SM_H_VPL_MAX;  // 1 or 4 waves
+  if (N <= 64 * v14) {
     wpr = 1;
-  } else if (N <= 256 * 64) {
+  } else if (N <= 256 * v14) {
     wpr = 4;
   } else if (N <= 1024 * (vec ? 64 : 32)) {
     wpr = 16;

@@ -117,6 +117,22 @@ KNOBS = {
                                       "b1h16_n16384_d128_bf16_sigma3_causal",
                                       "b4h16_n1024_d128_bf16", "b8h12_n3000_d128_bf16"],
                            what="waves per dK/dV workgroup at d=128 (32 keys each)"),
+    "sm_nontemporal": dict(macro="ATTN_CFG_SM_NONTEMPORAL", values=[1, 0], pass_="softmax",
+                           workloads=["sm_m32768_n4096_bf16", "sm_m8192_n16384_bf16",
+                                      "sm_m32768_n4096_f32"],
+                           what="the row softmax's one-pass loads and stores with the "
+                                "non-temporal hint (1) or plain (0)"),
+    "sm_f32_vpl": dict(macro="ATTN_CFG_SM_F32_VPL_MAX", values=[16, 32, 64], pass_="softmax",
+                       workloads=["sm_m32768_n4096_f32", "sm_m65536_n2048_f32",
+                                  "sm_m8192_n16384_f32", "sm_m16384_n8192_f32"],
+                       what="fp32 values per lane a one- or four-wave softmax row holds "
+                            "(fewer: more waves per row)"),
+    "sm_h_vpl": dict(macro="ATTN_CFG_SM_H_VPL_MAX", values=[32, 64, 16], pass_="softmax",
+                     workloads=["sm_m32768_n4096_bf16", "sm_m65536_n2048_bf16",
+                                "sm_m8192_n16384_bf16", "sm_m262144_n512_bf16",
+                                "sm_m16384_n8192_f16"],
+                     what="16-bit values per lane a one- or four-wave softmax row holds "
+                          "(fewer: more waves per row)"),
     "bwd_lookahead": dict(macro="ATTN_CFG_BWD_LOOKAHEAD", values=[2, 1], pass_="bwd",
                           workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16"],
                           what="MFMA steps by which the backward's LDS operand reads run ahead "
@@ -187,8 +203,19 @@ def build_all(jobs=4, knobs=None):
             print(msg, flush=True)
 
 
+class SoftmaxWorkload:
+    """An M x N row-softmax problem, named sm_m<M>_n<N>_<dtype>."""
+
+    def __init__(self, name):
+        m, n, dt = name.split("_")[1:]
+        self.name, self.M, self.N, self.dtype = name, int(m[1:]), int(n[1:]), dt
+        self.d = None
+
+
 def _workload(name):
     from .inputs import WORKLOADS, Workload
+    if name.startswith("sm_"):
+        return SoftmaxWorkload(name)
     if name in WORKLOADS:
         return WORKLOADS[name]
     if name == "b1h32_n8192_d128_bf16_causal":
@@ -218,8 +245,11 @@ def _runner(lib, w, pass_, tensors):
     import torch
     from . import binding
     q, k, v, o, lse, dout, grads, ws, qs = tensors
-    dt = {"bf16": binding.ATTN_BF16, "f16": binding.ATTN_F16}[w.dtype]
+    dt = {"bf16": binding.ATTN_BF16, "f16": binding.ATTN_F16, "f32": binding.ATTN_F32}[w.dtype]
     stream = torch.cuda.current_stream().cuda_stream
+    if pass_ == "softmax":  # q is x, o is y
+        return lambda: lib.attn_row_softmax(q.data_ptr(), w.N, o.data_ptr(), w.N, w.M, w.N, dt,
+                                            dt, stream)
     if pass_ == "fwd":
         return lambda: lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                     lse.data_ptr(), w.B, w.H, w.N, w.d, int(w.causal), w.scale, dt,
@@ -246,6 +276,57 @@ def _runner(lib, w, pass_, tensors):
     raise ValueError(pass_)
 
 
+def _softmax_input(w):
+    """x ~ N(0, 1), seeded, in the workload's dtype (on the CPU)."""
+    import torch
+    g = torch.Generator().manual_seed(1)
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[w.dtype]
+    return torch.randn(w.M, w.N, generator=g).to(tdt)
+
+
+def _time_and_compare(knob, kn, wl, names, calls, out, rounds, target_ms):
+    """Time every variant's call interleaved (median of `rounds` alternating
+    rounds of ~target_ms each), then compare each one's outputs with the
+    shipped library's. Returns one result row per variant."""
+    import torch
+
+    def timed(n, count):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(count):
+            calls[n]()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / count
+
+    ms1 = timed(names[0], 3)
+    per = max(3, int(target_ms / max(ms1, 1e-3)))
+    for n in names:  # warm every variant, then time them in alternating order
+        timed(n, per)
+    times = {n: [] for n in names}
+    for r in range(rounds):
+        for n in (names if r % 2 == 0 else names[::-1]):
+            times[n].append(timed(n, per))
+    rows, ref = [], None
+    base = sorted(times[names[0]])[rounds // 2]
+    for n in names:
+        for x in out:
+            x.zero_()
+        assert calls[n]() == 0
+        torch.cuda.synchronize()
+        got = [x.clone() for x in out]
+        if ref is None:
+            ref = got
+        diff = max(float((a.float() - b.float()).abs().max()) for a, b in zip(got, ref))
+        med = sorted(times[n])[len(times[n]) // 2]
+        rows.append(dict(knob=knob, macro=kn["macro"], value=kn["values"][names.index(n)],
+                         shipped=n == names[0], workload=wl, pass_=kn["pass_"],
+                         us=med * 1e3, rel=base / med - 1.0, max_abs_diff_vs_shipped=diff))
+        print("%-18s %-10s %-40s %9.1f us  %+6.2f%%  diff %.1e" % (
+            knob, rows[-1]["value"], wl, med * 1e3, 100 * rows[-1]["rel"], diff), flush=True)
+    return rows
+
+
 def run_all(rounds=8, target_ms=60.0, knobs=None):
     import torch
     from . import binding
@@ -259,6 +340,13 @@ def run_all(rounds=8, target_ms=60.0, knobs=None):
         for wl in kn["workloads"]:
             w = _workload(wl)
             dev = torch.device("cuda:0")
+            if kn["pass_"] == "softmax":
+                x = _softmax_input(w).to(dev)
+                y = torch.empty_like(x)
+                tensors = (x, None, None, y, None, None, None, None, None)
+                calls = {n: _runner(libs[n], w, "softmax", tensors) for n in names}
+                results += _time_and_compare(knob, kn, wl, names, calls, [y], rounds, target_ms)
+                continue
             q, k, v = (x.to(dev) for x in workload_qkv(w, seed=0))
             dout = make_dout(w.B, w.H, w.N, w.d, w.dtype, seed=0).to(dev)
             o = torch.empty(q.shape, dtype=torch.float32, device=dev)
@@ -276,43 +364,7 @@ def run_all(rounds=8, target_ms=60.0, knobs=None):
             tensors = (q, k, v, o, lse, dout, grads, ws, qs)
             calls = {n: _runner(libs[n], w, kn["pass_"], tensors) for n in names}
             out = grads if kn["pass_"] == "bwd" else [o, lse]
-
-            def timed(n, count):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(count):
-                    calls[n]()
-                e1.record()
-                torch.cuda.synchronize()
-                return e0.elapsed_time(e1) / count
-
-            ms1 = timed(names[0], 3)
-            per = max(3, int(target_ms / max(ms1, 1e-3)))
-            for n in names:  # warm every variant, then time them in alternating order
-                timed(n, per)
-            times = {n: [] for n in names}
-            for r in range(rounds):
-                for n in (names if r % 2 == 0 else names[::-1]):
-                    times[n].append(timed(n, per))
-            ref = None
-            base = sorted(times[names[0]])[rounds // 2]
-            for n in names:
-                for x in out:
-                    x.zero_()
-                assert calls[n]() == 0
-                torch.cuda.synchronize()
-                got = [x.clone() for x in out]
-                if ref is None:
-                    ref = got
-                diff = max(float((a - b).abs().max()) for a, b in zip(got, ref))
-                med = sorted(times[n])[len(times[n]) // 2]
-                results.append(dict(knob=knob, macro=kn["macro"], value=kn["values"][names.index(n)],
-                                    shipped=n == names[0], workload=wl, pass_=kn["pass_"],
-                                    us=med * 1e3, rel=base / med - 1.0,
-                                    max_abs_diff_vs_shipped=diff))
-                print("%-18s %-10s %-40s %9.1f us  %+6.2f%%  diff %.1e" % (
-                    knob, results[-1]["value"], wl, med * 1e3, 100 * results[-1]["rel"], diff),
-                    flush=True)
+            results += _time_and_compare(knob, kn, wl, names, calls, out, rounds, target_ms)
     with open(os.path.join(SWEEP_DIR, "results.json"), "w") as f:
         json.dump(results, f, indent=1)
     return results

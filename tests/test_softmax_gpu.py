@@ -56,6 +56,10 @@ SHAPES = [
     (4, 20000, "f16", 1.0), (2, 65536, "bf16", 2.0), (3, 32767, "f32", 1.0),
     # two passes, 16-byte loads
     (2, 70000, "bf16", 1.0),
+    # one wave up to 2048 16-bit / 1024 fp32 columns, four waves up to 8192 / 4096
+    (6, 2048, "bf16", 1.0), (5, 2056, "bf16", 1.0), (7, 2049, "f16", 1.0),
+    (3, 8192, "f16", 1.0), (3, 8200, "bf16", 1.0), (9, 1024, "f32", 1.0),
+    (9, 1028, "f32", 1.0), (4, 4096, "f32", 2.0), (4, 4100, "f32", 1.0),
 ]
 
 

@@ -68,7 +68,11 @@ def test_workloads_resolve():
     for knob, kn in sweep.KNOBS.items():
         for wl in kn["workloads"]:
             w = sweep._workload(wl)
-            assert w.name == wl and w.d in (64, 128)
+            if kn["pass_"] == "softmax":
+                assert w.name == wl and w.M >= 1 and w.N >= 1 and w.dtype in ("bf16", "f16", "f32")
+                assert "sm_m%d_n%d_%s" % (w.M, w.N, w.dtype) == wl
+            else:
+                assert w.name == wl and w.d in (64, 128)
 
 
 def test_markdown_table():
