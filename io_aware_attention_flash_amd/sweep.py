@@ -127,6 +127,12 @@ KNOBS = {
                                   "sm_m8192_n16384_f32", "sm_m16384_n8192_f32"],
                        what="fp32 values per lane a one- or four-wave softmax row holds "
                             "(fewer: more waves per row)"),
+    "sm_packed": dict(macro="ATTN_CFG_SM_PACKED", values=[0, 1], pass_="softmax",
+                      workloads=["sm_m32768_n4096_bf16", "sm_m8192_n16384_bf16",
+                                 "sm_m4096_n65536_f16", "sm_m16384_n32768_bf16",
+                                 "sm_m262144_n512_bf16"],
+                      what="16-bit softmax rows held packed as loaded, each exponential "
+                           "taken twice (1), or held as fp32 exponentials (0)"),
     "sm_h_vpl": dict(macro="ATTN_CFG_SM_H_VPL_MAX", values=[32, 64, 16], pass_="softmax",
                      workloads=["sm_m32768_n4096_bf16", "sm_m65536_n2048_bf16",
                                 "sm_m8192_n16384_bf16", "sm_m262144_n512_bf16",
