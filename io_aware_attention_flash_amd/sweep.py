@@ -107,6 +107,11 @@ KNOBS = {
                                          "b1h16_n16384_d128_bf16_sigma3_causal"],
                               what="bf16 V converted to fp16 by a first pass from this N on "
                                    "(2^30: never)"),
+    "bwd_o_nontemporal": dict(macro="ATTN_CFG_BWD_O_NONTEMPORAL", values=[0, 1], pass_="bwd",
+                              workloads=["b2h32_n4096_d128_bf16_causal", "b8h12_n3000_d64_f16",
+                                         "b4h16_n1024_d64_bf16"],
+                              what="the dQ kernel's loads of O (read once, for D) with the "
+                                   "non-temporal hint (1) or plain (0)"),
     "bwd_dq_tile_k": dict(macro="ATTN_CFG_BWD_DQ_TILE_K", values=[64, 32, 128], pass_="bwd",
                           workloads=["b2h32_n4096_d128_bf16_causal",
                                      "b8h12_n3000_d64_f16"],
