@@ -123,3 +123,37 @@ def test_offsets_past_2_31(M, N, dt):
         _check(y[r:r + 1], x[r:r + 1].cpu(), dt, "row %d of %d" % (r, M))
     del x, y
     torch.cuda.empty_cache()
+
+
+def _random_cases(n, seed=2027):
+    rng = np.random.default_rng(seed)
+    pairs = [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("f16", "f16"), ("f16", "f32")]
+    cases = []
+    for i in range(n):
+        M = int(rng.integers(1, 300))
+        N = int(round(np.exp(rng.uniform(0.0, np.log(150000.0)))))
+        if N * M > (1 << 25):
+            M = max(1, (1 << 25) // N)
+        tin, tout = pairs[int(rng.integers(0, len(pairs)))]
+        pad = int(rng.choice([0, 0, 8, 13]))  # extra row stride (elements) of x and y
+        cases.append((i, M, N, tin, tout, pad, float(rng.choice([1.0, 3.0]))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(40),
+                         ids=lambda c: "%02d_M%dN%d_%s_%s_pad%d_s%g" % c)
+def test_row_softmax_random(case):
+    """Seeded draws of M, N (log-uniform up to 150000: every kernel shape and
+    both passes), dtype pair and row padding (16-byte pieces or element
+    loads), against the oracle."""
+    i, M, N, tin, tout, pad, sigma = case
+    print("case", case, flush=True)
+    x = _x(M, N, tin, sigma, seed=500 + i)
+    xg = torch.zeros(M, N + pad, dtype=DT[tin], device=DEV)
+    xg[:, :N] = x.to(DEV)
+    ybuf = torch.zeros(M, N + pad, dtype=DT[tout], device=DEV)
+    y = binding.row_softmax(xg[:, :N], out_dtype=DT[tout], out=ybuf[:, :N])
+    torch.cuda.synchronize()
+    _check(y, x, tout, "random %s" % (case,))
+    if pad:
+        assert torch.count_nonzero(ybuf[:, N:]) == 0, "wrote past the row"
